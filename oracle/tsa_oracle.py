@@ -1,0 +1,221 @@
+"""Oracle for Token Sparse Attention's per-layer path: plain, slow, float64, CPU only.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may import this module.  It shares no code with the HIP library and imports
+nothing from it; the two meet only through the seeded inputs of ``workloads.py``.
+
+What it computes, stage by stage, in the order the method runs (sources: the skill page
+"Token Sparse Attention Long Context", Steps 1-3, and the paper page "Token Sparse
+Attention: Efficient Long-Context Inference with Interleaved Token Selection",
+Figure 3 and the Abstract):
+
+1. ``score``     -- per query head h, the causal softmax(q k^T / sqrt(d)) rows of the
+                    last W query positions, summed over those rows: one importance
+                    score per key position (skill page, Step 1, the query-key
+                    alignment scorer, restricted to the last W causal rows).
+2. ``select``    -- the per-head subset S_h: the first ``n_sink`` positions and the
+                    last W positions always, plus the highest-scoring other positions
+                    up to ``keep`` in total; equal scores go to the lower position;
+                    S_h is returned in ascending position order (skill page, Step 1,
+                    top-K selection; Figure 3's per-head subset).
+3. ``gather``    -- Q^, K^, V^ = the rows of Q, K, V at S_h; query head h reads KV
+                    head floor(h / G) (skill page, Step 2; Figure 3, stage 1).
+4. ``attend``    -- dense causal softmax attention on the compact rows (skill page,
+                    Step 3; Figure 3, stage 2; the Abstract's compatibility with dense
+                    attention kernels).
+5. ``scatter_residual`` -- the compact outputs put back at their positions, zero at
+                    every other position, and the residual added everywhere (Figure 3:
+                    scatter back to the full layout, then add the residual).
+
+Every function works in float64; bf16 and fp32 inputs widen to float64 exactly.
+The readings taken where the pages are silent (window, causality, ties, order, the
+residual everywhere, the GQA head map, scale 1/sqrt(head_dim)) are stated at each
+function.  Non-finite inputs are rejected.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "window", "forced_positions", "score", "score_head", "select", "select_row",
+    "gather", "attend", "attend_rows", "scatter_residual", "forward", "threshold",
+]
+
+
+def _f64(x) -> np.ndarray:
+    a = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("oracle inputs must be finite")
+    return a
+
+
+def window(L: int, W: int) -> int:
+    """Number of scoring query rows: the last W positions, clipped to the sequence."""
+    return min(W, L)
+
+
+def forced_positions(L: int, W: int, n_sink: int) -> np.ndarray:
+    """Positions every head keeps: sinks [0, n_sink) and the window [L-W, L), as a set
+    union clipped to [0, L), ascending."""
+    Wp = window(L, W)
+    f = set(range(min(n_sink, L))) | set(range(L - Wp, L))
+    return np.array(sorted(f), dtype=np.int64)
+
+
+def score_head(qh: np.ndarray, kg: np.ndarray, W: int, scale: float) -> np.ndarray:
+    """Scores of one (batch, query head): qh [L,d], kg [L,d] (its KV head) -> [L].
+
+    Row i in [L-W', L) gives z_ij = scale * <q_i, k_j> for j <= i and the softmax over
+    those j; the score of key j is the sum of its weights over the rows (skill page,
+    Step 1: softmax along keys, summed along queries, logits divided by sqrt(d)).
+    """
+    L = qh.shape[0]
+    Wp = window(L, W)
+    rows = np.arange(L - Wp, L)
+    z = scale * (qh[rows] @ kg.T)                       # [W', L]
+    z[np.arange(L)[None, :] > rows[:, None]] = -np.inf   # causal: key j visible to row i iff j <= i
+    z -= z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    return p.sum(axis=0)
+
+
+def score(q, k, W: int, scale: float | None = None) -> np.ndarray:
+    """Scores for all heads: q [B,L,H,d], k [B,L,Hkv,d] -> s [B,H,L] (float64).
+
+    Query head h uses KV head floor(h / G), G = H / Hkv (consecutive query heads share a
+    KV head)."""
+    q, k = _f64(q), _f64(k)
+    B, L, H, d = q.shape
+    Hkv = k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    s = np.empty((B, H, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s[b, h] = score_head(q[b, :, h, :], k[b, :, h // G, :], W, scale)
+    return s
+
+
+def select_row(s_row, keep: int, W: int, n_sink: int) -> np.ndarray:
+    """S_h for one head from its scores [L]: forced positions, then the best other
+    positions by (higher score, then lower position) until ``keep`` are held; returned
+    ascending (skill page, Step 1, top-K selection)."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    L = s_row.shape[0]
+    F = forced_positions(L, W, n_sink)
+    if not (len(F) <= keep <= L):
+        raise ValueError(f"keep={keep} outside [{len(F)}, {L}]")
+    is_forced = np.zeros(L, dtype=bool)
+    is_forced[F] = True
+    cand = np.nonzero(~is_forced)[0]
+    order = np.lexsort((cand, -s_row[cand]))   # primary: score descending; secondary: position ascending
+    chosen = cand[order[: keep - len(F)]]
+    return np.sort(np.concatenate([F, chosen]))
+
+
+def select(s, keep: int, W: int, n_sink: int) -> np.ndarray:
+    """idx [B,H,keep] (int64, strictly ascending per head) from scores [B,H,L]."""
+    s = np.asarray(s, dtype=np.float64)
+    B, H, _ = s.shape
+    idx = np.empty((B, H, keep), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            idx[b, h] = select_row(s[b, h], keep, W, n_sink)
+    return idx
+
+
+def threshold(s_row, keep: int, W: int, n_sink: int) -> float:
+    """The score of the last non-forced position taken (the (keep-|F|)-th best), or +inf
+    when no non-forced position is taken."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    L = s_row.shape[0]
+    F = forced_positions(L, W, n_sink)
+    n = keep - len(F)
+    if n <= 0:
+        return float("inf")
+    mask = np.ones(L, dtype=bool)
+    mask[F] = False
+    return float(np.sort(s_row[mask])[::-1][n - 1])
+
+
+def gather(q, k, v, idx):
+    """Q^[b,h,t] = Q[b,S_t,h]; K^[b,h,t] = K[b,S_t,g]; V^[b,h,t] = V[b,S_t,g], g = h // G
+    (skill page, Step 2, gather by index; Figure 3, stage 1).  -> three [B,H,keep,d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, L, H, d = q.shape
+    G = H // k.shape[2]
+    keep = idx.shape[2]
+    qh = np.empty((B, H, keep, d))
+    kh = np.empty((B, H, keep, d))
+    vh = np.empty((B, H, keep, d))
+    for b in range(B):
+        for h in range(H):
+            sel = idx[b, h]
+            qh[b, h] = q[b, sel, h, :]
+            kh[b, h] = k[b, sel, h // G, :]
+            vh[b, h] = v[b, sel, h // G, :]
+    return qh, kh, vh
+
+
+def _attend_head(qh, kh, vh, scale, rows):
+    out = np.empty((len(rows), qh.shape[1]))
+    # Causal softmax attention, a block of query rows at a time (never a full keep x keep matrix).
+    blk = 128
+    for a in range(0, len(rows), blk):
+        rr = rows[a:a + blk]
+        hi = int(rr.max()) + 1
+        z = scale * (qh[rr] @ kh[:hi].T)                         # [nr, hi]
+        z[np.arange(hi)[None, :] > rr[:, None]] = -np.inf        # compact position u visible to t iff u <= t
+        z -= z.max(axis=1, keepdims=True)
+        p = np.exp(z)
+        p /= p.sum(axis=1, keepdims=True)
+        out[a:a + len(rr)] = p @ vh[:hi]
+    return out
+
+
+def attend(qh, kh, vh, scale: float | None = None) -> np.ndarray:
+    """O^[b,h,t] = sum over u <= t of softmax_u(scale <Q^_t, K^_u>) V^_u (skill page,
+    Step 3; Figure 3, stage 2).  Causality on compact positions equals causality on the
+    original positions because S_h is ascending."""
+    qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
+    B, H, n, d = qh.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    oh = np.empty_like(qh)
+    rows = np.arange(n)
+    for b in range(B):
+        for h in range(H):
+            oh[b, h] = _attend_head(qh[b, h], kh[b, h], vh[b, h], scale, rows)
+    return oh
+
+
+def attend_rows(qh_bh, kh_bh, vh_bh, rows, scale: float) -> np.ndarray:
+    """Compact attention of one (batch, head) at the given compact rows only -> [len(rows), d]."""
+    return _attend_head(_f64(qh_bh), _f64(kh_bh), _f64(vh_bh), float(scale), np.asarray(rows, dtype=np.int64))
+
+
+def scatter_residual(oh, idx, r) -> np.ndarray:
+    """Out[b,p,h] = R[b,p,h] + O^[b,h,rank(p)] if p is in S_h, else R[b,p,h] (the compact
+    outputs scattered into a zero full-length tensor, then the residual added: Figure 3,
+    stage 2; skill page, Step 2)."""
+    oh, r = _f64(oh), _f64(r)
+    out = r.copy()
+    B, H, n, _ = oh.shape
+    for b in range(B):
+        for h in range(H):
+            out[b, idx[b, h], h, :] += oh[b, h]
+    return out
+
+
+def forward(q, k, v, r, keep: int, W: int, n_sink: int, scale: float | None = None) -> dict:
+    """All five stages; returns scores, idx, the compact tensors, O^ and Out."""
+    d = np.asarray(q).shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    s = score(q, k, W, scale)
+    idx = select(s, keep, W, n_sink)
+    qh, kh, vh = gather(q, k, v, idx)
+    oh = attend(qh, kh, vh, scale)
+    out = scatter_residual(oh, idx, r)
+    return {"scores": s, "idx": idx, "qh": qh, "kh": kh, "vh": vh, "oh": oh, "out": out}

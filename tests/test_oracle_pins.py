@@ -1,0 +1,250 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each test ties one oracle stage to what the pages and the mathematics fix:
+hand-worked exact cases, a closed form, a library routine (torch's scaled dot-product
+attention in float64, which also fixes the grouped-query head map), brute force on tiny
+inputs, and invariants of the definition.  Together they are chosen so that a dropped
+scale, a non-causal mask, a wrong window, a wrong KV head, a wrong tie order, a
+score-ordered subset, a missing sink or a residual added in the wrong places fails at
+least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _num(x):
+    if isinstance(x, str):
+        if x == "sqrt2ln2":
+            return math.sqrt(2.0) * math.log(2.0)
+        return float(Fraction(x))
+    return float(x)
+
+
+def _arr(rows):
+    return np.array([[_num(c) for c in row] for row in rows], dtype=np.float64)
+
+
+def _hand_inputs(case):
+    g = json.load(open(GOLDEN))
+    c, e = g["common"], g[case]
+    L, d = c["L"], c["d"]
+    q = np.zeros((1, L, 1, d))
+    k = np.zeros((1, L, 1, d))
+    for p, row in e["q_nonzero"].items():
+        q[0, int(p), 0] = [_num(x) for x in row]
+    for p, row in e["k_nonzero"].items():
+        k[0, int(p), 0] = [_num(x) for x in row]
+    v = _arr(c["v"]).reshape(1, L, 1, d)
+    r = _arr(c["r"]).reshape(1, L, 1, d)
+    return c, e, q, k, v, r
+
+
+@pytest.mark.parametrize("case", ["case1", "case2"])
+def test_hand_cases_exact(case):
+    c, e, q, k, v, r = _hand_inputs(case)
+    res = oracle.forward(q, k, v, r, keep=c["keep"], W=c["W"], n_sink=c["n_sink"])
+    np.testing.assert_allclose(res["scores"][0, 0], [_num(x) for x in e["scores"]], rtol=0, atol=1e-15)
+    assert res["idx"][0, 0].tolist() == e["idx"]
+    np.testing.assert_allclose(res["oh"][0, 0], _arr(e["oh"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(res["out"][0, :, 0], _arr(e["out"]), rtol=0, atol=1e-14)
+
+
+def _harmonic(n):
+    return sum(1.0 / m for m in range(1, n + 1))
+
+
+@pytest.mark.parametrize("L,W,n_sink,keep", [(64, 8, 4, 20), (50, 50, 0, 50), (33, 1, 3, 10)])
+def test_zero_query_closed_form(L, W, n_sink, keep):
+    # q = 0: row i spreads weight 1/(i+1) over keys 0..i, so s_j = H_L - H_{max(j, L-W')}.
+    rng = np.random.default_rng(1)
+    d = 4
+    q = np.zeros((1, L, 2, d))
+    k = rng.standard_normal((1, L, 1, d))
+    s = oracle.score(q, k, W)
+    Wp = min(W, L)
+    want = np.array([_harmonic(L) - _harmonic(max(j, L - Wp)) for j in range(L)])
+    np.testing.assert_allclose(s[0, 0], want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(s[0, 1], want, rtol=0, atol=1e-13)
+    # Every key before the window ties, so the lowest positions fill the budget.
+    idx = oracle.select(s, keep, W, n_sink)
+    expect = sorted(set(range(keep - Wp)) | set(range(L - Wp, L)))
+    assert idx[0, 0].tolist() == expect
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def _sdpa(q_blhd, k_blhd, v_blhd, scale=None):
+    """torch SDPA (float64, CPU, causal, grouped-query) on [B,L,H,d] tensors -> [B,L,H,dv]."""
+    qt = _t(q_blhd).permute(0, 2, 1, 3)
+    kt = _t(k_blhd).permute(0, 2, 1, 3)
+    vt = _t(v_blhd).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d", [(2, 4, 2, 37, 16), (1, 8, 2, 64, 8), (1, 3, 3, 9, 5)])
+def test_keep_all_equals_dense_sdpa(B, H, Hkv, L, d):
+    # keep = L: S_h = [0, L), so Out - R is plain causal attention ("sparse equals dense").
+    x = workloads.small_random(B, H, Hkv, L, d, seed=7)
+    res = oracle.forward(x["q"], x["k"], x["v"], x["r"], keep=L, W=3, n_sink=2)
+    assert all((res["idx"][b, h] == np.arange(L)).all() for b in range(B) for h in range(H))
+    want = _sdpa(x["q"].astype(np.float64), x["k"].astype(np.float64), x["v"].astype(np.float64))
+    np.testing.assert_allclose(res["out"] - x["r"], want, rtol=0, atol=1e-12)
+
+
+def test_attend_matches_sdpa_on_subset():
+    x = workloads.small_random(1, 4, 2, 60, 16, seed=3)
+    res = oracle.forward(x["q"], x["k"], x["v"], x["r"], keep=21, W=4, n_sink=2)
+    # SDPA on the compact tensors ([B,H,keep,d] -> [B,keep,H,d] view).
+    qh, kh, vh = (np.transpose(t, (0, 2, 1, 3)) for t in (res["qh"], res["kh"], res["vh"]))
+    want = _sdpa(qh, kh, vh)
+    np.testing.assert_allclose(np.transpose(res["oh"], (0, 2, 1, 3)), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,W", [(1, 4, 2, 24, 8, 5), (2, 6, 3, 17, 4, 17), (1, 2, 1, 12, 6, 40)])
+def test_score_matches_sdpa_probabilities(B, H, Hkv, L, d, W):
+    # With V = identity (one-hot value rows), SDPA returns the causal probability rows
+    # themselves; the score is their sum over the last W' rows.
+    x = workloads.small_random(B, H, Hkv, L, d, seed=11)
+    eye = np.broadcast_to(np.eye(L)[None, :, None, :], (B, L, Hkv, L)).copy()
+    P = _sdpa(x["q"].astype(np.float64), x["k"].astype(np.float64), eye)   # [B, L(query), H, L(key)]
+    Wp = min(W, L)
+    want = P[:, L - Wp:, :, :].sum(axis=1)                                  # [B, H, L]
+    s = oracle.score(x["q"], x["k"], W)
+    np.testing.assert_allclose(s, want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(s.sum(axis=-1), Wp, rtol=0, atol=1e-12)   # each row's weights sum to 1
+
+
+def _check_subset(s_row, S, keep, W, n_sink):
+    L = len(s_row)
+    S = list(S)
+    assert len(S) == keep
+    assert all(a < b for a, b in zip(S, S[1:]))
+    Fset = set(range(min(n_sink, L))) | set(range(L - min(W, L), L))
+    assert Fset <= set(S)
+    chosen = [c for c in S if c not in Fset]
+    unchosen = [u for u in range(L) if u not in set(S)]
+    for c in chosen:            # brute-force exchange property of top-k with ties to the lower position
+        for u in unchosen:
+            assert s_row[c] > s_row[u] or (s_row[c] == s_row[u] and c < u)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_select_exchange_property(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(6, 40))
+    W = int(rng.integers(1, 6))
+    n_sink = int(rng.integers(0, 5))
+    nF = len(oracle.forced_positions(L, W, n_sink))
+    keep = int(rng.integers(nF, L + 1))
+    s = np.round(rng.random(L) * 4) / 4          # few distinct values: many ties
+    s[:n_sink] = 0.0                              # sinks score lowest but must stay
+    S = oracle.select_row(s, keep, W, n_sink)
+    _check_subset(s, S, keep, W, n_sink)
+
+
+def test_select_edge_cases():
+    s = np.linspace(1.0, 0.0, 10)
+    assert oracle.select_row(s, 10, 3, 2).tolist() == list(range(10))            # keep = L
+    assert oracle.select_row(s, 5, 3, 2).tolist() == [0, 1, 7, 8, 9]            # keep = |F|
+    assert oracle.select_row(s, 10, 64, 4).tolist() == list(range(10))          # W >= L: everything forced
+    assert oracle.select_row(s, 4, 2, 2).tolist() == [0, 1, 8, 9]
+    assert oracle.select_row(np.zeros(6), 6, 2, 8).tolist() == list(range(6))    # sinks beyond L clip
+    with pytest.raises(ValueError):
+        oracle.select_row(s, 4, 3, 2)                                            # keep < |F|
+    with pytest.raises(ValueError):
+        oracle.select_row(s, 11, 3, 2)                                           # keep > L
+
+
+def test_gather_scatter_brute_force():
+    x = workloads.small_random(2, 4, 2, 9, 3, seed=5)
+    idx = np.array([[[0, 2, 5, 8], [1, 2, 3, 8], [0, 4, 7, 8], [3, 5, 6, 8]]] * 2)
+    qh, kh, vh = oracle.gather(x["q"], x["k"], x["v"], idx)
+    oh = np.random.default_rng(0).standard_normal(qh.shape)
+    out = oracle.scatter_residual(oh, idx, x["r"])
+    for b in range(2):
+        for h in range(4):
+            for t in range(4):
+                p = int(idx[b, h, t])
+                for c in range(3):
+                    assert qh[b, h, t, c] == x["q"][b, p, h, c]
+                    assert kh[b, h, t, c] == x["k"][b, p, h // 2, c]
+                    assert vh[b, h, t, c] == x["v"][b, p, h // 2, c]
+            for p in range(9):
+                for c in range(3):
+                    want = float(x["r"][b, p, h, c])
+                    if p in idx[b, h].tolist():
+                        want += oh[b, h, idx[b, h].tolist().index(p), c]
+                    assert out[b, p, h, c] == want
+
+
+def test_attention_special_values():
+    rng = np.random.default_rng(2)
+    n, d = 17, 6
+    qh = rng.standard_normal((1, 1, n, d))
+    vh = rng.standard_normal((1, 1, n, d))
+    # K^ = 0: uniform causal weights, a running mean of V^.
+    oh = oracle.attend(qh, np.zeros_like(qh), vh)
+    want = np.cumsum(vh[0, 0], axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(oh[0, 0], want, rtol=0, atol=1e-14)
+    # V^ constant: any convex combination returns it.
+    c = rng.standard_normal(d)
+    oh = oracle.attend(qh, rng.standard_normal((1, 1, n, d)), np.broadcast_to(c, (1, 1, n, d)))
+    np.testing.assert_allclose(oh[0, 0], np.broadcast_to(c, (n, d)), rtol=0, atol=1e-14)
+
+
+def test_unselected_rows_equal_residual_bitwise():
+    x = workloads.small_random(1, 4, 2, 40, 8, seed=9, dtype="bf16")
+    res = oracle.forward(x["q"], x["k"], x["v"], x["r"], keep=12, W=4, n_sink=2)
+    for h in range(4):
+        mask = np.ones(40, dtype=bool)
+        mask[res["idx"][0, h]] = False
+        assert np.array_equal(res["out"][0, mask, h], x["r"][0, mask, h].astype(np.float64))
+        assert not np.array_equal(res["out"][0, ~mask, h], x["r"][0, ~mask, h].astype(np.float64))
+
+
+def test_attend_rows_matches_attend():
+    x = workloads.small_random(1, 2, 1, 30, 8, seed=4)
+    res = oracle.forward(x["q"], x["k"], x["v"], x["r"], keep=14, W=3, n_sink=1)
+    rows = [0, 5, 13]
+    o = oracle.attend_rows(res["qh"][0, 1], res["kh"][0, 1], res["vh"][0, 1], rows, 1 / np.sqrt(8))
+    np.testing.assert_allclose(o, res["oh"][0, 1, rows], rtol=0, atol=1e-15)
+
+
+def test_planted_tokens_recovered_small():
+    # A reduced planted workload: every planted key should be selected by every head
+    # of its KV group (the planted keys align with the window queries).
+    w = workloads.WORKLOADS["bf16_L64k_planted"].with_(B=1, L=4096, keep=409)
+    x = workloads.make_inputs(w)
+    s = oracle.score(x["q"], x["k"], w.W)
+    idx = oracle.select(s, w.keep, w.W, w.n_sink)
+    for g in range(w.Hkv):
+        P = set(x["planted"][(0, g)].tolist())
+        for h in range(g * w.G, (g + 1) * w.G):
+            assert len(P & set(idx[0, h].tolist())) == len(P)
+
+
+def test_inputs_reproducible_and_bf16_exact():
+    a = workloads.small_random(1, 2, 1, 5000, 4, seed=3, dtype="bf16")
+    b = workloads.small_random(1, 2, 1, 5000, 4, seed=3, dtype="bf16")
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["r"], b["r"])
+    assert np.array_equal(workloads.round_bf16(a["k"]), a["k"])
+    t = torch.from_numpy(np.ascontiguousarray(a["v"])).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(t, a["v"])          # bf16-exact values survive torch's conversion
+    raw = np.random.default_rng(0).standard_normal(1000, dtype=np.float32)
+    want = torch.from_numpy(raw).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(workloads.round_bf16(raw), want)   # our RNE equals torch's
