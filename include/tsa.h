@@ -1,0 +1,158 @@
+/*
+ * tsa.h -- C ABI of the token-sparse attention library (libtsa.so), gfx950 only.
+ *
+ * The library runs one attention layer of Token Sparse Attention: every query head
+ * scores the keys, keeps a subset S_h of them, runs dense causal attention on the
+ * compact subset and scatters the result back to full length with the residual added.
+ * Sources: the skill page "Token Sparse Attention Long Context" (Core Concept,
+ * Architecture Overview, Steps 1-3) and the paper page "Token Sparse Attention:
+ * Efficient Long-Context Inference with Interleaved Token Selection" (Abstract,
+ * Figure 3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Sizes (tsa_desc):  B batch, H query heads, Hkv KV heads (H % Hkv == 0, G = H / Hkv),
+ *   L sequence length, d head dim (64 or 128), keep = |S_h| per query head, W score
+ *   window, n_sink sink tokens, dtype of q/k/v/residual/out and of the compact
+ *   tensors, scale of the logits (0 means 1/sqrt(d)).
+ * Grouped-query map: query head h reads KV head g(h) = h / G.
+ * Layouts (contiguous, row-major, element strides implied by the sizes):
+ *   q, residual, out, o        [B][L][H][d]      (dtype)
+ *   k, v                        [B][L][Hkv][d]    (dtype)
+ *   scores                      [B][H][L]         (fp32)
+ *   idx                         [B][H][keep]      (int32, strictly ascending per head)
+ *   qh, kh, vh, oh              [B][H][keep][d]   (dtype; compact per-head tensors)
+ * Memory and ownership: every pointer is a device pointer allocated by the caller and
+ *   aligned to 16 bytes; the library allocates and frees nothing, keeps no pointer
+ *   after a call returns, and holds no mutable global state.  Scratch space comes from
+ *   the caller's workspace (ws, ws_bytes), sized by tsa_workspace_size.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call only enqueues work on it and returns; nothing synchronises, nothing copies
+ *   between host and device.  Results are deterministic (no floating-point atomics).
+ * Errors: arguments are validated on the host before anything is enqueued; on a
+ *   validation error the call returns the status and writes nothing.  TSA_ERR_LAUNCH
+ *   reports a failed kernel launch.  Faults inside kernels surface at the caller's
+ *   next synchronisation.  Inputs must be finite; non-finite values give unspecified
+ *   (but memory-safe) results.
+ */
+#ifndef TSA_H_
+#define TSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSA_ABI_VERSION 1
+#define TSA_MAX_W 64 /* largest score window the scoring kernel holds in registers */
+
+typedef enum {
+  TSA_OK = 0,
+  TSA_ERR_NULL = 1,      /* a required pointer is NULL */
+  TSA_ERR_SHAPE = 2,     /* a size <= 0, H % Hkv != 0, d not 64/128, or sizes past index limits */
+  TSA_ERR_BUDGET = 3,    /* keep < |forced set| or keep > L, W < 1 or W > TSA_MAX_W, n_sink < 0 */
+  TSA_ERR_DTYPE = 4,     /* dtype not TSA_F32 / TSA_BF16 */
+  TSA_ERR_ALIGN = 5,     /* a pointer not 16-byte aligned */
+  TSA_ERR_WORKSPACE = 6, /* ws_bytes smaller than tsa_workspace_size, or ws NULL when needed */
+  TSA_ERR_ALIAS = 7,     /* an output overlaps an input it must not overlap */
+  TSA_ERR_LAUNCH = 8,    /* a kernel launch failed */
+  TSA_ERR_ARG = 9        /* an enum argument (op) out of range, or scale not finite / negative */
+} tsa_status;
+
+typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum { TSA_OP_SCORE = 0, TSA_OP_SELECT = 1, TSA_OP_SCATTER = 2, TSA_OP_FORWARD = 3 } tsa_op;
+
+typedef struct {
+  int32_t B, H, Hkv, L, d;
+  int32_t keep;   /* |S_h|, the number of positions each query head keeps */
+  int32_t W;      /* score window: the last min(W, L) query positions score the keys */
+  int32_t n_sink; /* positions [0, n_sink) are always kept */
+  int32_t dtype;  /* tsa_dtype */
+  float scale;    /* logit scale; 0 selects 1/sqrt(d) */
+} tsa_desc;
+
+/* Returns TSA_ABI_VERSION. */
+int tsa_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* tsa_status_str(int status);
+
+/* Host-only validation of a descriptor (no HIP call).  Forced set
+ * F = [0, min(n_sink, L)) U [L - min(W, L), L); keep must satisfy |F| <= keep <= L. */
+tsa_status tsa_check(const tsa_desc* desc);
+
+/* Host-only: bytes of workspace the call `op` needs for `desc` (written to *bytes). */
+tsa_status tsa_workspace_size(const tsa_desc* desc, int op, size_t* bytes);
+
+/* Token scoring (skill page, Step 1: query-key alignment scores, softmax over keys
+ * summed over queries; restricted here to the last W' = min(W, L) query rows, causal).
+ * For every (b, h) and key j:
+ *   scores[b][h][j] = sum over rows i in [L-W', L), i >= j, of
+ *                     softmax_j'( scale * <q[b][i][h], k[b][j'][g(h)]> ), j' <= i,
+ * evaluated at j.  Products accumulate in fp32, probabilities and sums are fp32.
+ * In: q, k.  Out: scores.  Workspace: tsa_workspace_size(TSA_OP_SCORE). */
+tsa_status tsa_score(const tsa_desc* desc, const void* q, const void* k, float* scores,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Top-K selection (skill page, Step 1, selection of the top-scoring tokens; the paper
+ * page's Figure 3 per-head subset S_h).  Per (b, h): S_h = F plus the keep - |F|
+ * non-forced positions with the largest scores, equal scores going to the lower
+ * position; written ascending to idx[b][h][0..keep).  Scores must be >= 0 (as
+ * tsa_score produces).  In: scores.  Out: idx.  Workspace: TSA_OP_SELECT (0 bytes:
+ * ws may be NULL). */
+tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Gather-compression (skill page, Step 2, gathering the selected tokens; Figure 3,
+ * stage 1):  qh[b][h][t] = q[b][idx[b][h][t]][h],  kh[b][h][t] = k[b][idx][g(h)],
+ * vh[b][h][t] = v[b][idx][g(h)].  Bit-exact copies.  idx entries must lie in [0, L).
+ * The outputs must not overlap the inputs. */
+tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* idx, void* qh, void* kh, void* vh, void* stream);
+
+/* Dense causal attention on the compact rows (skill page, Step 3; Figure 3, stage 2):
+ *   oh[b][h][t] = sum over u <= t of softmax_u( scale * <qh[b][h][t], kh[b][h][u]> ) vh[b][h][u],
+ * fp32 accumulation and online softmax, result rounded once to dtype.  Because S_h is
+ * ascending, the causal mask on compact rows equals the mask on original positions.
+ * oh must not overlap qh, kh or vh. */
+tsa_status tsa_attn(const tsa_desc* desc, const void* qh, const void* kh, const void* vh,
+                    void* oh, void* stream);
+
+/* Scatter-decompression plus residual (skill page, Step 2, scattering back to the full
+ * sequence; Figure 3: scatter into the full layout, then add the residual):
+ *   out[b][p][h] = residual[b][p][h] + oh[b][h][t]   if p = idx[b][h][t],
+ *   out[b][p][h] = residual[b][p][h]                 (bit-exact) otherwise.
+ * The sum is formed in fp32 and rounded once (round to nearest even).  out == residual
+ * (exactly the same pointer) updates in place and touches only the kept rows; any other
+ * overlap of out with residual, oh or idx is TSA_ERR_ALIAS.  Workspace: TSA_OP_SCATTER
+ * (an inverse position map for the out-of-place pass; 0 bytes in place). */
+tsa_status tsa_scatter_residual(const tsa_desc* desc, const void* oh, const int32_t* idx,
+                                const void* residual, void* out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* The whole layer in one call on one stream: score -> select -> gather -> attention ->
+ * scatter + residual (the skill page's Core Concept compress/decompress sequence;
+ * Figure 3, both stages).  scores_opt / idx_opt, when not NULL, receive the scores and
+ * the subsets; otherwise they live in the workspace.  out may equal residual (in place).
+ * Workspace: TSA_OP_FORWARD. */
+tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const void* v,
+                       const void* residual, void* out, float* scores_opt, int32_t* idx_opt,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Dense causal attention over all L positions with grouped-query heads, the library's
+ * own full-attention reference (the paper page's Abstract: the method composes with
+ * dense attention kernels).  o[b][i][h] = sum over j <= i of
+ * softmax_j(scale * <q[b][i][h], k[b][j][g(h)]>) v[b][j][g(h)].  keep, W and n_sink
+ * are ignored.  o must not overlap q, k or v. */
+tsa_status tsa_dense_attn(const tsa_desc* desc, const void* q, const void* k, const void* v,
+                          void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H_ */

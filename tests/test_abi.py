@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point that
+include/tsa.h declares, and rejects bad arguments on the host before launching anything.
+Pointers here are fake addresses: validation fails before any memory is touched."""
+import ctypes
+
+import pytest
+
+from tests._lib import ensure_built
+
+tsa = ensure_built()
+L = tsa.lib()
+
+EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_check", "tsa_dense_attn", "tsa_forward", "tsa_gather_qkv",
+            "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_status_str", "tsa_workspace_size"]
+
+
+def D(**kw):
+    base = dict(B=1, H=32, Hkv=8, L=8192, d=128, keep=4096, W=64, n_sink=4, dtype=tsa.TSA_BF16, scale=0.0)
+    base.update(kw)
+    return tsa.make_desc(**base)
+
+
+def test_header_declares_and_library_exports_every_entry_point():
+    declared = tsa.header_functions()
+    assert declared == EXPECTED
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.tsa_abi_version() == 1
+    assert L.tsa_status_str(7) and L.tsa_status_str(1234) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(dtype=7), 4),
+    (dict(H=0), 2), (dict(Hkv=3), 2), (dict(d=96), 2), (dict(L=-1), 2), (dict(B=-2), 2),
+    (dict(keep=67), 3),            # |F| = 4 + 64 = 68
+    (dict(keep=68), 0),
+    (dict(keep=8193), 3),
+    (dict(keep=8192), 0),
+    (dict(W=0), 3), (dict(W=65), 3), (dict(n_sink=-1), 3),
+    (dict(scale=-1.0), 9), (dict(scale=float("nan")), 9),
+    (dict(L=40, keep=40, W=64), 0),            # window covers the whole sequence
+    (dict(L=40, keep=39, W=64), 3),
+    (dict(L=0, keep=0), 0),                    # empty problem: nothing to do
+    (dict(B=0), 0),
+    (dict(B=4096, H=32), 2),                   # grid limit
+])
+def test_check_codes(kw, code):
+    assert tsa.tsa_check(D(**kw)) == code
+
+
+def test_workspace_sizes():
+    d = D()
+    assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) == 0
+    assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SCATTER) == 32 * 8192 * 4
+    fwd = tsa.tsa_workspace_size(d, tsa.TSA_OP_FORWARD)
+    assert fwd >= 4 * 32 * 4096 * 128 * 2 + 2 * 32 * 8192 * 4
+    assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SCORE) > 0
+    with pytest.raises(tsa.TsaError) as e:
+        tsa.tsa_workspace_size(d, 17)
+    assert e.value.status == 9
+    with pytest.raises(tsa.TsaError):
+        tsa.tsa_workspace_size(D(keep=3), tsa.TSA_OP_FORWARD)
+
+
+A = 1 << 40           # fake, well-separated, 16-byte aligned addresses
+GB = 1 << 32
+
+
+def call(name, *args):
+    return getattr(L, name)(*args)
+
+
+def test_entry_points_reject_before_launch():
+    d = D()
+    bd = ctypes.byref(d)
+    q, k, v, r, o = A, A + GB, A + 2 * GB, A + 3 * GB, A + 4 * GB
+    qh, kh, vh, oh = A + 5 * GB, A + 6 * GB, A + 7 * GB, A + 8 * GB
+    idx, sc, ws = A + 9 * GB, A + 10 * GB, A + 11 * GB
+    big = 1 << 34
+    # NULL pointers
+    assert call("tsa_score", bd, None, k, sc, ws, big, None) == 1
+    assert call("tsa_select", bd, sc, None, None, 0, None) == 1
+    assert call("tsa_gather_qkv", bd, q, k, v, idx, qh, kh, None, None) == 1
+    assert call("tsa_attn", bd, qh, kh, None, oh, None) == 1
+    assert call("tsa_scatter_residual", bd, oh, idx, None, o, ws, big, None) == 1
+    assert call("tsa_forward", bd, q, k, v, r, None, None, None, ws, big, None) == 1
+    assert call("tsa_dense_attn", bd, q, k, v, None, None) == 1
+    # misaligned
+    assert call("tsa_gather_qkv", bd, q + 8, k, v, idx, qh, kh, vh, None) == 5
+    assert call("tsa_attn", bd, qh, kh, vh, oh + 4, None) == 5
+    assert call("tsa_forward", bd, q, k, v, r, o, sc + 2, None, ws, big, None) == 5
+    # workspace
+    assert call("tsa_score", bd, q, k, sc, ws, 16, None) == 6
+    assert call("tsa_score", bd, q, k, sc, None, big, None) == 6
+    assert call("tsa_scatter_residual", bd, oh, idx, r, o, ws, 16, None) == 6
+    assert call("tsa_forward", bd, q, k, v, r, o, None, None, ws, 1024, None) == 6
+    # aliasing
+    assert call("tsa_gather_qkv", bd, q, k, v, idx, q + 4096, kh, vh, None) == 7
+    assert call("tsa_gather_qkv", bd, q, k, v, idx, qh, qh + 4096, vh, None) == 7
+    assert call("tsa_attn", bd, qh, kh, vh, qh, None) == 7
+    assert call("tsa_scatter_residual", bd, oh, idx, r, r + 256, ws, big, None) == 7   # partial overlap
+    assert call("tsa_scatter_residual", bd, oh, idx, r, oh, ws, big, None) == 7
+    assert call("tsa_forward", bd, q, k, v, r, q, None, None, ws, big, None) == 7
+    assert call("tsa_forward", bd, q, k, v, r, o, None, None, k, big, None) == 7
+    assert call("tsa_dense_attn", bd, q, k, v, v, None) == 7
+    assert call("tsa_score", bd, q, k, q, ws, big, None) == 7
+    # descriptor errors come first
+    bad = ctypes.byref(D(keep=2))
+    assert call("tsa_forward", bad, q, k, v, r, o, None, None, ws, big, None) == 3
+    assert call("tsa_dense_attn", ctypes.byref(D(d=32)), q, k, v, o, None) == 2
+    assert call("tsa_dense_attn", ctypes.byref(D(keep=2)), None, None, None, None, None) == 1   # keep ignored
+    assert call("tsa_forward", None, q, k, v, r, o, None, None, ws, big, None) == 1

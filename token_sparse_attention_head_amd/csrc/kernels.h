@@ -1,0 +1,27 @@
+// Host-side launchers of the token-sparse attention kernels (internal to libtsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "tsa.h"
+
+namespace tsa {
+
+// Key chunking of the scoring passes (shared by the launcher and workspace sizing).
+void score_chunking(const tsa_desc& d, int& chunk, int& nchunk);
+
+hipError_t launch_score(const tsa_desc& d, const void* q, const void* k, float* scores, float2* part, float2* stat,
+                        hipStream_t s);
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, hipStream_t s);
+hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                             void* qh, void* kh, void* vh, hipStream_t s);
+hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh, const void* vh, void* oh,
+                               hipStream_t s);
+hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
+                             hipStream_t s);
+hipError_t launch_build_inverse(const tsa_desc& d, const int32_t* idx, int32_t* inv, hipStream_t s);
+hipError_t launch_scatter_residual(const tsa_desc& d, const void* oh, const int32_t* inv, const void* res, void* out,
+                                   hipStream_t s);
+hipError_t launch_scatter_inplace(const tsa_desc& d, const void* oh, const int32_t* idx, void* out, hipStream_t s);
+
+}  // namespace tsa

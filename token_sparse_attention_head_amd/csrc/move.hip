@@ -1,0 +1,177 @@
+// Data-movement kernels: gather-compression of Q/K/V into the compact per-head tensors
+// and scatter-decompression of the attention output with the residual added.
+//
+// Gather follows the skill page "Token Sparse Attention Long Context", Step 2 (rows of
+// the selected tokens copied into a dense block), and the paper page "Token Sparse
+// Attention: Efficient Long-Context Inference with Interleaved Token Selection",
+// Figure 3, stage 1 (per-head compact Q, K, V).  Scatter follows the same Step 2
+// (outputs put back at their original positions, zeros elsewhere) and Figure 3,
+// stage 2 (scatter into the full layout, then add the residual).
+//
+// Every thread moves 16-byte vectors; one row of d elements is 128-512 bytes, so a
+// wave reads and writes whole 128-byte lines.  Kept rows are read once per query head;
+// the out-of-place scatter streams residual and out once in memory order.
+#include "common.h"
+#include "kernels.h"
+
+namespace tsa {
+
+namespace {
+
+template <int ROWB>
+__global__ __launch_bounds__(256) void gather_qkv_kernel(const char* __restrict__ q, const char* __restrict__ k,
+                                                         const char* __restrict__ v, const int32_t* __restrict__ idx,
+                                                         char* __restrict__ qh, char* __restrict__ kh,
+                                                         char* __restrict__ vh, int H, int G, int L, int keep) {
+  constexpr int CH = ROWB / 16;
+  const int bh = blockIdx.y;                  // b * H + h
+  const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+  const int t = e / CH;
+  const int c = e % CH;
+  if (t >= keep) return;
+  const int h = bh % H;
+  const int64_t b = bh / H;
+  const int Hkv = H / G;
+  const int64_t crow = (int64_t)bh * keep + t;
+  const int p = idx[crow];
+  const int64_t qoff = ((b * L + p) * H + h) * ROWB + c * 16;
+  const int64_t kvoff = ((b * L + p) * Hkv + h / G) * ROWB + c * 16;
+  const u32x4 a = ld16(q + qoff);
+  const u32x4 kk = ld16(k + kvoff);
+  const u32x4 vv = ld16(v + kvoff);
+  const int64_t o = crow * ROWB + c * 16;
+  st16(qh + o, a);
+  st16(kh + o, kk);
+  st16(vh + o, vv);
+}
+
+// 16 bytes of residual plus 16 bytes of attention output, summed in fp32, rounded once.
+__device__ __forceinline__ u32x4 add_rows(u32x4 r, u32x4 o, tsa_dtype dt) {
+  u32x4 out;
+  if (dt == TSA_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_to_f32(r[i] & 0xFFFFu) + bf16_to_f32(o[i] & 0xFFFFu);
+      const float hi = bf16_to_f32(r[i] >> 16) + bf16_to_f32(o[i] >> 16);
+      out[i] = pack_bf16x2(lo, hi);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __float_as_uint(__uint_as_float(r[i]) + __uint_as_float(o[i]));
+  }
+  return out;
+}
+
+// Out-of-place: one pass over [B][L][H] rows in memory order.  inv[b][h][p] is the
+// compact row of position p in S_h, or -1.
+template <int ROWB, tsa_dtype DT>
+__global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __restrict__ oh,
+                                                               const int32_t* __restrict__ inv,
+                                                               const char* __restrict__ res, char* __restrict__ out,
+                                                               int H, int L, int keep) {
+  constexpr int CH = ROWB / 16;
+  const int64_t b = blockIdx.y;
+  const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t row = e / CH;                // p * H + h
+  const int c = e % CH;
+  if (row >= (uint32_t)L * (uint32_t)H) return;
+  const int p = row / H;
+  const int h = row % H;
+  const int64_t off = ((b * L + p) * H + h) * ROWB + c * 16;
+  const u32x4 r = ld16_nt(res + off);
+  const int t = inv[(b * H + h) * L + p];
+  u32x4 o = r;
+  if (t >= 0) o = add_rows(r, ld16(oh + (((b * H + h) * keep + t) * ROWB + c * 16)), DT);
+  st16_nt(out + off, o);
+}
+
+// In place (out == residual): only the kept rows are read and rewritten.
+template <int ROWB, tsa_dtype DT>
+__global__ __launch_bounds__(256) void scatter_add_inplace_kernel(const char* __restrict__ oh,
+                                                                  const int32_t* __restrict__ idx, char* out, int H,
+                                                                  int L, int keep) {
+  constexpr int CH = ROWB / 16;
+  const int bh = blockIdx.y;
+  const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+  const int t = e / CH;
+  const int c = e % CH;
+  if (t >= keep) return;
+  const int h = bh % H;
+  const int64_t b = bh / H;
+  const int64_t crow = (int64_t)bh * keep + t;
+  const int p = idx[crow];
+  char* dst = out + ((b * L + p) * H + h) * ROWB + c * 16;
+  st16(dst, add_rows(ld16(dst), ld16(oh + crow * ROWB + c * 16), DT));
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(int32_t* __restrict__ p, int64_t n, int32_t value) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = value;
+}
+
+__global__ __launch_bounds__(256) void invert_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ inv,
+                                                     int L, int keep) {
+  const int bh = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= keep) return;
+  const int p = idx[(int64_t)bh * keep + t];
+  inv[(int64_t)bh * L + p] = t;
+}
+
+inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+}  // namespace
+
+#define TSA_ROWB_DISPATCH(ROWB_VAL, ...)            \
+  switch (ROWB_VAL) {                               \
+    case 128: { constexpr int RB = 128; __VA_ARGS__; break; } \
+    case 256: { constexpr int RB = 256; __VA_ARGS__; break; } \
+    case 512: { constexpr int RB = 512; __VA_ARGS__; break; } \
+    default: return hipErrorInvalidValue;           \
+  }
+
+hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                             void* qh, void* kh, void* vh, hipStream_t s) {
+  const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
+  const dim3 grid(blocks_for((int64_t)d.keep * (rowb / 16)), d.B * d.H);
+  TSA_ROWB_DISPATCH(rowb, gather_qkv_kernel<RB><<<grid, 256, 0, s>>>(
+                              (const char*)q, (const char*)k, (const char*)v, idx, (char*)qh, (char*)kh, (char*)vh,
+                              d.H, d.H / d.Hkv, d.L, d.keep));
+  return hipGetLastError();
+}
+
+hipError_t launch_build_inverse(const tsa_desc& d, const int32_t* idx, int32_t* inv, hipStream_t s) {
+  const int64_t n = (int64_t)d.B * d.H * d.L;
+  const unsigned fb = (unsigned)std::min<int64_t>(blocks_for(n), 4096);
+  fill_kernel<<<fb, 256, 0, s>>>(inv, n, -1);
+  invert_kernel<<<dim3(blocks_for(d.keep), d.B * d.H), 256, 0, s>>>(idx, inv, d.L, d.keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_residual(const tsa_desc& d, const void* oh, const int32_t* inv, const void* res, void* out,
+                                   hipStream_t s) {
+  const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
+  const dim3 grid(blocks_for((int64_t)d.L * d.H * (rowb / 16)), d.B);
+  if (d.dtype == TSA_BF16) {
+    TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_BF16><<<grid, 256, 0, s>>>(
+                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
+  } else {
+    TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_F32><<<grid, 256, 0, s>>>(
+                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_inplace(const tsa_desc& d, const void* oh, const int32_t* idx, void* out, hipStream_t s) {
+  const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
+  const dim3 grid(blocks_for((int64_t)d.keep * (rowb / 16)), d.B * d.H);
+  if (d.dtype == TSA_BF16) {
+    TSA_ROWB_DISPATCH(rowb, scatter_add_inplace_kernel<RB, TSA_BF16><<<grid, 256, 0, s>>>(
+                                (const char*)oh, idx, (char*)out, d.H, d.L, d.keep));
+  } else {
+    TSA_ROWB_DISPATCH(rowb, scatter_add_inplace_kernel<RB, TSA_F32><<<grid, 256, 0, s>>>(
+                                (const char*)oh, idx, (char*)out, d.H, d.L, d.keep));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,258 @@
+// Per-head token scoring on MFMA.
+//
+// The skill page "Token Sparse Attention Long Context", Step 1, scores a key by the
+// softmax(q k^T / sqrt(d)) weight it receives, summed over queries; the paper page
+// "Token Sparse Attention: Efficient Long-Context Inference with Interleaved Token
+// Selection" asks for a lightweight score (TL;DR, Abstract).  This library restricts
+// the sum to the last W' = min(W, L) query rows of each query head, with the causal
+// mask, so scoring costs O(W' L d) instead of O(L^2 d):
+//
+//   s[b,h,j] = sum_{i in [L-W', L), i >= j} exp(z_ij - m_i) / l_i,
+//   z_ij = scale <q_i, k_j>,  m_i = max_{j<=i} z_ij,  l_i = sum_{j<=i} exp(z_ij - m_i).
+//
+// Pass 1 (one wave per (b, h, key chunk)): z on MFMA with keys as rows and window
+// queries as columns, so each lane owns one query and a running (max, sum) over its
+// keys.  A merge kernel folds the chunks into (m_i, 1/l_i).  Pass 2 recomputes z with
+// window queries as rows and keys as columns, so each lane owns one key and sums its
+// probabilities over the window rows in a fixed order (the same order for every key,
+// so equal inputs give bit-equal scores).  Probabilities and sums stay fp32.
+//
+// Operands come straight from global memory: a lane reads one contiguous half of a
+// head-dim row (128 bytes at d = 128 bf16), so no LDS staging is needed; the waves of a
+// workgroup are the query heads of one KV group on the same key chunk, so the key rows
+// they share are read once from HBM.
+#include "common.h"
+#include "kernels.h"
+
+namespace tsa {
+
+namespace {
+
+constexpr float NEG_BIG = -3.0e38f;
+
+struct ScoreGeom {
+  int B, H, G, Hkv, L, Wp, chunk, nchunk;
+  int64_t q_row, k_row;  // element strides between consecutive positions
+};
+
+// Wave unit -> (b, h, chunk); heads of one KV group are consecutive units.
+__device__ __forceinline__ bool unit_of(const ScoreGeom& g, int unit, int& b, int& h, int& ch) {
+  const int hh = unit % g.G;
+  int rest = unit / g.G;
+  ch = rest % g.nchunk;
+  rest /= g.nchunk;
+  if (rest >= g.B * g.Hkv) return false;
+  const int kvh = rest % g.Hkv;
+  b = rest / g.Hkv;
+  h = kvh * g.G + hh;
+  return true;
+}
+
+template <typename T, int D, int RB>
+__device__ __forceinline__ void load_window_q(const T* q, const ScoreGeom& g, int b, int h, int lane,
+                                              HalfRow<T, D> (&qf)[RB]) {
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = rb * 32 + (lane & 31);
+    if (row < g.Wp) {
+      const int64_t i = g.L - g.Wp + row;
+      qf[rb].load(q + ((int64_t)b * g.L + i) * g.q_row + (int64_t)h * D + hf * (D / 2));
+    } else {
+      qf[rb].zero();
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_key(const T* k, const ScoreGeom& g, int b, int kvh, int j, int lane,
+                                         HalfRow<T, D>& kf) {
+  if (j < g.L)
+    kf.load(k + ((int64_t)b * g.L + j) * g.k_row + (int64_t)kvh * D + (lane >> 5) * (D / 2));
+  else
+    kf.zero();
+}
+
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(256) void score_pass1_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          float2* __restrict__ part, ScoreGeom g, float c) {
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+  int b, h, ch;
+  if (!unit_of(g, blockIdx.x * 4 + threadIdx.x / TSA_WAVE, b, h, ch)) return;
+  const int kvh = h / g.G;
+
+  HalfRow<T, D> qf[RB];
+  load_window_q<T, D, RB>(q, g, b, h, lane, qf);
+
+  float m[RB], s[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) { m[rb] = NEG_BIG; s[rb] = 0.f; }
+
+  const int j_beg = ch * g.chunk;
+  const int j_end = min(g.L, j_beg + g.chunk);
+  const int first_row_pos = g.L - g.Wp;
+  for (int j0 = j_beg; j0 < j_end; j0 += 32) {
+    HalfRow<T, D> kf;
+    load_key<T, D>(k, g, b, kvh, j0 + (lane & 31), lane, kf);
+    const bool need_mask = j0 + 31 > first_row_pos;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x16 acc = {};
+      acc = dot_tile<T, D>(acc, kf, qf[rb]);     // rows: keys, columns: window queries
+      const int i = first_row_pos + rb * 32 + (lane & 31);
+      float tmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + acc_row(r, hf);
+        if (need_mask && j > i) acc[r] = -__builtin_huge_valf();   // masked: contributes exp2(-inf) = 0
+        tmax = fmaxf(tmax, acc[r]);
+      }
+      // m stays finite (starts at NEG_BIG), so a fully masked tile leaves (m, s) unchanged.
+      const float mn = fmaxf(m[rb], tmax * c);
+      float add = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mn));
+      s[rb] = s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + add;
+      m[rb] = mn;
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float mo = xor32(m[rb]);
+    const float so = xor32(s[rb]);
+    const float M = fmaxf(m[rb], mo);
+    const float S = s[rb] * __builtin_amdgcn_exp2f(m[rb] - M) + so * __builtin_amdgcn_exp2f(mo - M);
+    const int row = rb * 32 + (lane & 31);
+    if (hf == 0 && row < g.Wp)
+      part[(((int64_t)b * g.H + h) * g.nchunk + ch) * g.Wp + row] = make_float2(M, S);
+  }
+}
+
+// Folds the per-chunk (max, sum) of every window row into (m_i, 1 / l_i), in chunk order.
+__global__ __launch_bounds__(64) void score_merge_kernel(const float2* __restrict__ part, float2* __restrict__ stat,
+                                                         int nchunk, int Wp) {
+  const int bh = blockIdx.x;
+  const int row = threadIdx.x;
+  if (row >= Wp) return;
+  const float2* p = part + (int64_t)bh * nchunk * Wp + row;
+  float M = NEG_BIG;
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[(int64_t)c * Wp].x);
+  float S = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const float2 v = p[(int64_t)c * Wp];
+    S += v.y * __builtin_amdgcn_exp2f(v.x - M);
+  }
+  stat[(int64_t)bh * Wp + row] = make_float2(M, 1.0f / S);
+}
+
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(256) void score_pass2_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const float2* __restrict__ stat, float* __restrict__ scores,
+                                                          ScoreGeom g, float c) {
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+  int b, h, ch;
+  if (!unit_of(g, blockIdx.x * 4 + threadIdx.x / TSA_WAVE, b, h, ch)) return;
+  const int kvh = h / g.G;
+
+  HalfRow<T, D> qf[RB];
+  load_window_q<T, D, RB>(q, g, b, h, lane, qf);
+
+  // Row statistics of the 16 window rows this lane holds in each 32-row block.
+  float mrow[RB][16], il[RB][16];
+  const float2* st = stat + ((int64_t)b * g.H + h) * g.Wp;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb * 32 + acc_row(r, hf);
+      if (row < g.Wp) {
+        const float2 v = st[row];
+        mrow[rb][r] = v.x;
+        il[rb][r] = v.y;
+      } else {
+        mrow[rb][r] = __builtin_huge_valf();   // exp2(z - inf) = 0
+        il[rb][r] = 0.f;
+      }
+    }
+
+  const int j_beg = ch * g.chunk;
+  const int j_end = min(g.L, j_beg + g.chunk);
+  const int first_row_pos = g.L - g.Wp;
+  float* out = scores + ((int64_t)b * g.H + h) * g.L;
+  for (int j0 = j_beg; j0 < j_end; j0 += 32) {
+    HalfRow<T, D> kf;
+    const int j = j0 + (lane & 31);
+    load_key<T, D>(k, g, b, kvh, j, lane, kf);
+    const bool need_mask = j0 + 31 > first_row_pos;
+    float col = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x16 acc = {};
+      acc = dot_tile<T, D>(acc, qf[rb], kf);     // rows: window queries, columns: keys
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = first_row_pos + rb * 32 + acc_row(r, hf);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mrow[rb][r])) * il[rb][r];
+        if (need_mask && j > i) p = 0.f;
+        col += p;
+      }
+    }
+    col += xor32(col);
+    if (hf == 0 && j < g.L) out[j] = col;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_score_t(const tsa_desc& d, const void* q, const void* k, float* scores, float2* part,
+                          float2* stat, hipStream_t s) {
+  ScoreGeom g;
+  g.B = d.B; g.H = d.H; g.Hkv = d.Hkv; g.G = d.H / d.Hkv; g.L = d.L;
+  g.Wp = d.W < d.L ? d.W : d.L;
+  score_chunking(d, g.chunk, g.nchunk);
+  g.q_row = (int64_t)d.H * D;
+  g.k_row = (int64_t)d.Hkv * D;
+  const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)D);
+  const float c = scale * TSA_LOG2E;
+  const int units = d.B * d.H * g.nchunk;
+  const unsigned blocks = (unsigned)((units + 3) / 4);
+  if (g.Wp > 32) {
+    score_pass1_kernel<T, D, 2><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, part, g, c);
+  } else {
+    score_pass1_kernel<T, D, 1><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, part, g, c);
+  }
+  score_merge_kernel<<<d.B * d.H, 64, 0, s>>>(part, stat, g.nchunk, g.Wp);
+  if (g.Wp > 32) {
+    score_pass2_kernel<T, D, 2><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, stat, scores, g, c);
+  } else {
+    score_pass2_kernel<T, D, 1><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, stat, scores, g, c);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void score_chunking(const tsa_desc& d, int& chunk, int& nchunk) {
+  // About 4096 waves in flight over the whole problem, at least 32 keys per wave.
+  const int64_t keys_per_wave = ((int64_t)d.B * d.H * d.L + 4095) / 4096;
+  int64_t ck = (keys_per_wave + 31) / 32 * 32;
+  if (ck < 32) ck = 32;
+  if (ck > d.L) ck = (d.L + 31) / 32 * 32;
+  chunk = (int)ck;
+  nchunk = (int)((d.L + ck - 1) / ck);
+}
+
+hipError_t launch_score(const tsa_desc& d, const void* q, const void* k, float* scores, float2* part, float2* stat,
+                        hipStream_t s) {
+  if (d.dtype == TSA_BF16) {
+    if (d.d == 128) return launch_score_t<__bf16, 128>(d, q, k, scores, part, stat, s);
+    if (d.d == 64) return launch_score_t<__bf16, 64>(d, q, k, scores, part, stat, s);
+  } else {
+    if (d.d == 128) return launch_score_t<float, 128>(d, q, k, scores, part, stat, s);
+    if (d.d == 64) return launch_score_t<float, 64>(d, q, k, scores, part, stat, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tsa

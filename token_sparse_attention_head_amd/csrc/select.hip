@@ -1,0 +1,179 @@
+// Top-K token selection per (batch, query head): the subset S_h, ascending.
+//
+// The skill page "Token Sparse Attention Long Context", Step 1, keeps the top-scoring
+// tokens of each head; the paper page "Token Sparse Attention: Efficient Long-Context
+// Inference with Interleaved Token Selection", Figure 3, calls the result the per-head
+// token subset.  This library fixes what the pages leave open: the sink positions
+// [0, n_sink) and the window [L-W', L) are always kept, the remaining budget goes to
+// the highest scores with ties to the lower position, and S_h is written in ascending
+// position order.
+//
+// One 1024-thread workgroup per (b, h) row.  Scores are >= 0, so their fp32 bit
+// patterns order like the values.  The threshold T (the score of the last candidate
+// taken) is found by a three-pass radix select (11 + 11 + 10 bits) with LDS
+// histograms; then every wave compacts a contiguous segment of the row with wave
+// ballots and mbcnt prefix counts, ties at T going to the lowest positions.
+#include "common.h"
+#include "kernels.h"
+
+namespace tsa {
+
+namespace {
+
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / TSA_WAVE;
+constexpr int SEL_MAX_BINS = 2048;
+
+// Inclusive scan of one value per thread over the whole workgroup.
+__device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* wave_tot) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / TSA_WAVE;
+#pragma unroll
+  for (int o = 1; o < TSA_WAVE; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, TSA_WAVE);
+    if (lane >= o) x += y;
+  }
+  if (lane == TSA_WAVE - 1) wave_tot[wave] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  __syncthreads();
+  return x + before;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __restrict__ scores,
+                                                             int32_t* __restrict__ idx, int32_t* __restrict__ inv,
+                                                             int L, int keep, int c0, int c1) {
+  // Candidates are the positions [c0, c1); [0, c0) and [c1, L) are forced.
+  __shared__ uint32_t hist[SEL_MAX_BINS];
+  __shared__ uint32_t wave_tot[SEL_WAVES];
+  __shared__ uint32_t found_bin, found_above;
+  __shared__ uint32_t seg_strict[SEL_WAVES], seg_eq[SEL_WAVES];
+  __shared__ uint32_t seg_out[SEL_WAVES], seg_eq_before[SEL_WAVES];
+
+  const int bh = blockIdx.x;
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)bh * L);
+  const int tid = threadIdx.x;
+  const int n_cand = c1 - c0;
+  const int n_forced = L - n_cand;
+  uint32_t need = (uint32_t)(keep - n_forced);   // candidates still to take
+  const bool take_all = (int)need >= n_cand;
+  const bool take_none = need == 0;
+
+  uint32_t T = 0xFFFFFFFFu;   // threshold key
+  uint32_t need_eq = 0;       // how many candidates equal to T are taken (lowest positions first)
+  if (!take_all && !take_none) {
+    uint32_t prefix = 0, pmask = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < nb; i += SEL_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (int j = c0 + tid; j < c1; j += SEL_THREADS) {
+        const uint32_t u = key[j];
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      // Bins in descending order; thread t owns ranks [t*per, (t+1)*per).
+      const int per = nb / SEL_THREADS;
+      uint32_t local = 0;
+      for (int q = 0; q < per; ++q) local += hist[nb - 1 - (tid * per + q)];
+      const uint32_t incl = block_inclusive_scan(local, wave_tot);
+      const uint32_t excl = incl - local;
+      if (excl < need && need <= incl) {
+        uint32_t cum = excl;
+        for (int q = 0; q < per; ++q) {
+          const int bin = nb - 1 - (tid * per + q);
+          if (cum + hist[bin] >= need) {
+            found_bin = bin;
+            found_above = cum;
+            break;
+          }
+          cum += hist[bin];
+        }
+      }
+      __syncthreads();
+      need -= found_above;
+      prefix |= found_bin << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      __syncthreads();
+    }
+    T = prefix;
+    need_eq = need;
+  }
+
+  // Compaction: wave w owns positions [w*seg, (w+1)*seg).
+  const int lane = lane_id();
+  const int wave = tid / TSA_WAVE;
+  const int seg = ((L + SEL_WAVES - 1) / SEL_WAVES + TSA_WAVE - 1) / TSA_WAVE * TSA_WAVE;
+  const int beg = wave * seg;
+  const int end = min(L, beg + seg);
+
+  auto classify = [&](int j, bool& strict, bool& eq) {
+    const bool valid = j < end;
+    const bool cand = valid && j >= c0 && j < c1;
+    uint32_t u = 0;
+    if (cand) u = key[j];
+    strict = (valid && !cand) || (cand && (take_all || (!take_none && u > T)));
+    eq = cand && !take_all && !take_none && u == T;
+  };
+
+  uint32_t n_strict = 0, n_eq = 0;
+  for (int base = beg; base < end; base += TSA_WAVE) {
+    bool s, e;
+    classify(base + lane, s, e);
+    n_strict += __popcll(__ballot(s));
+    n_eq += __popcll(__ballot(e));
+  }
+  if (lane == 0) {
+    seg_strict[wave] = n_strict;
+    seg_eq[wave] = n_eq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t eq_before = 0, out = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+      const uint32_t rem = need_eq > eq_before ? need_eq - eq_before : 0;
+      const uint32_t take_eq = min(rem, seg_eq[w]);
+      seg_eq_before[w] = eq_before;
+      seg_out[w] = out;
+      out += seg_strict[w] + take_eq;
+      eq_before += seg_eq[w];
+    }
+  }
+  __syncthreads();
+
+  int32_t* row_idx = idx + (int64_t)bh * keep;
+  int32_t* row_inv = inv ? inv + (int64_t)bh * L : nullptr;
+  uint32_t pos = seg_out[wave];
+  uint32_t eq_rank = seg_eq_before[wave];
+  for (int base = beg; base < end; base += TSA_WAVE) {
+    const int j = base + lane;
+    bool s, e;
+    classify(j, s, e);
+    const uint64_t emask = __ballot(e);
+    const uint32_t my_eq = eq_rank + __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0u));
+    const bool take = s || (e && my_eq < need_eq);
+    const uint64_t tmask = __ballot(take);
+    const uint32_t my_pos = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(tmask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)tmask, 0u));
+    if (take && my_pos < (uint32_t)keep) row_idx[my_pos] = j;
+    if (row_inv && j < end) row_inv[j] = (take && my_pos < (uint32_t)keep) ? (int32_t)my_pos : -1;
+    pos += __popcll(tmask);
+    eq_rank += __popcll(emask);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, hipStream_t s) {
+  const int Wp = d.W < d.L ? d.W : d.L;
+  const int c1 = d.L - Wp;
+  const int c0 = d.n_sink < c1 ? d.n_sink : c1;
+  select_kernel<<<d.B * d.H, SEL_THREADS, 0, s>>>(scores, idx, inv, d.L, d.keep, c0, c1);
+  return hipGetLastError();
+}
+
+}  // namespace tsa
