@@ -1,0 +1,262 @@
+"""Benchmark of one token-sparse attention layer (score -> select -> gather -> attention ->
+scatter + residual) on one MI355X, on seeded synthetic inputs resident in HBM.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
+                  [--no-cpu-baseline] [--no-dense]
+
+A step is one tsa_forward call (all five stages, out-of-place scatter) on the workload.
+Prints ONE JSON line: the headline is prefill tokens/s = B * L / step time at
+L = 131072 (bf16, 32 query / 8 KV heads, d = 128, W = 64, 4 sinks, keep ratio 0.5), with
+the per-stage times, the speedup over the library's own dense causal attention at the
+same L, the keep-ratio sweep (0.5 / 0.25 / 0.1), the roofline of the attention kernel
+(the dominant one) and the float64 oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix / vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="bf16_L128k_r0.5")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--stage-reps", type=int, default=5)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every library call uses."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, reps):
+        t = self.torch
+        s = t.cuda.current_stream()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        a.record(s)
+        for _ in range(reps):
+            fn()
+        b.record(s)
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def algorithmic(w):
+    """Work the method must do per stage (flops or bytes), as defined for the roofline."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, H, Hkv, L, d, K, W = w.B, w.H, w.Hkv, w.L, w.d, w.keep, min(w.W, w.L)
+    score_flops = 2.0 * B * H * d * sum(L - W + r + 1 for r in range(W)) * 2   # two passes over the window logits
+    return {
+        "score_flops": score_flops,
+        "score_bytes": B * Hkv * L * d * e + B * H * W * d * e + 4 * B * H * L,
+        "select_bytes": 4 * B * H * (L + K),
+        "gather_bytes": 2 * 3 * B * H * K * d * e + 4 * B * H * K,
+        "attn_flops": 2.0 * B * H * d * K * (K + 1),
+        "scatter_bytes": 2 * B * L * H * d * e + B * H * K * d * e + 4 * B * H * L,
+        "dense_flops": 2.0 * B * H * d * L * (L + 1),
+    }
+
+
+def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
+    desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink)
+    ws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(r)
+    B, L, H, D = q.shape
+
+    def step():
+        tsa.tsa_forward(desc, q, k, v, r, out, None, None, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_events = timer.run(step, steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Stage by stage through the standalone entry points, same sizes and buffers.
+    scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    idx = torch.empty(B, H, w.keep, dtype=torch.int32, device="cuda")
+    sws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCORE)), dtype=torch.uint8, device="cuda")
+    comp = [torch.empty(B, H, w.keep, D, dtype=dt, device="cuda") for _ in range(4)]
+    cws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCATTER)), dtype=torch.uint8, device="cuda")
+    stages = {
+        "score": lambda: tsa.tsa_score(desc, q, k, scores, sws),
+        "select": lambda: tsa.tsa_select(desc, scores, idx),
+        "gather": lambda: tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2]),
+        "attn": lambda: tsa.tsa_attn(desc, comp[0], comp[1], comp[2], comp[3]),
+        "scatter": lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r, out, cws),
+    }
+    stage_ms = {}
+    for name, fn in stages.items():
+        fn()
+        stage_ms[name] = timer.run(fn, reps)
+    # In-place scatter variant (out == residual touches only kept rows); on a copy.
+    r2 = r.clone()
+    stage_ms["scatter_inplace"] = timer.run(lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r2, r2), reps)
+    del r2
+
+    res = {"workload": w.name, "keep": w.keep, "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events,
+           "wall_ms_per_step": wall_ms, "tokens_per_s": B * L / (ms_events / 1e3), "stage_ms": stage_ms}
+    a = algorithmic(w)
+    res["stage_rate"] = {
+        "score_tflops": a["score_flops"] / (stage_ms["score"] * 1e-3) / 1e12,
+        "select_gbs": a["select_bytes"] / (stage_ms["select"] * 1e-3) / 1e9,
+        "gather_gbs": a["gather_bytes"] / (stage_ms["gather"] * 1e-3) / 1e9,
+        "attn_tflops": a["attn_flops"] / (stage_ms["attn"] * 1e-3) / 1e12,
+        "scatter_gbs": a["scatter_bytes"] / (stage_ms["scatter"] * 1e-3) / 1e9,
+    }
+    if with_dense:
+        o = torch.empty_like(q)
+        dense = lambda: tsa.tsa_dense_attn(desc, q, k, v, o)   # noqa: E731
+        dense()
+        dms = timer.run(dense, max(2, reps // 2))
+        res["dense_ms"] = dms
+        res["dense_tflops"] = a["dense_flops"] / (dms * 1e-3) / 1e12
+        res["speedup_vs_dense"] = dms / ms_events
+        res["attn_speedup_vs_dense"] = dms / stage_ms["attn"]
+        del o
+    del ws, comp, out
+    return res
+
+
+def cpu_baseline(w, x, budget_s=20.0):
+    """Time the float64 oracle on a bounded sample of the workload: one (batch, head)'s
+    scores, subset, gather and scatter in full, and compact attention rows sampled evenly
+    across the subset; the attention time is scaled by the causal row costs (row t costs
+    t + 1 key visits), the head time by the number of heads."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    b, h, G = 0, 0, w.G
+    t0 = time.perf_counter()
+    qb = x["q"][b, :, h, :].astype(np.float64)
+    kb = x["k"][b, :, h // G, :].astype(np.float64)
+    s = oracle.score_head(qb, kb, w.W, 1.0 / np.sqrt(w.d))
+    S = oracle.select_row(s, w.keep, w.W, w.n_sink)
+    qh, kh, vh = qb[S], kb[S], x["v"][b, S, h // G, :].astype(np.float64)
+    t_head = time.perf_counter() - t0
+    # Attention rows: grow the sample until it costs about half the budget.
+    n = w.keep
+    rows_total = n * (n + 1) / 2.0
+    nr, t_att, cost = 16, 0.0, 0.0
+    while True:
+        rows = np.unique(np.linspace(0, n - 1, nr).astype(np.int64))
+        t1 = time.perf_counter()
+        oracle.attend_rows(qh, kh, vh, rows, 1.0 / np.sqrt(w.d))
+        t_att = time.perf_counter() - t1
+        cost = float(np.sum(rows + 1))
+        if t_att > budget_s / 4 or nr >= n:
+            break
+        nr *= 2
+    t2 = time.perf_counter()
+    oracle.scatter_residual(np.zeros((1, 1, n, w.d)), S[None, None], x["r"][b:b + 1, :, h:h + 1, :])
+    t_scatter = time.perf_counter() - t2
+    per_head = t_head + t_scatter + t_att * rows_total / cost
+    total = per_head * w.B * w.H
+    return {"value": w.B * w.L / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: head (b=0,h=0) score+select+gather+scatter in full, {len(rows)} of {n} compact "
+                      f"attention rows evenly spaced, scaled by causal row cost and by {w.B * w.H} heads; "
+                      f"{t_head + t_att + t_scatter:.1f} s of CPU work",
+            "seconds_per_step_extrapolated": total}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer shards by KV-head group with no "
+              "exchange, so one GPU's share is the measured unit", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import token_sparse_attention_head_amd as tsa
+    import workloads
+
+    if not os.path.exists(tsa.LIB_PATH):
+        from token_sparse_attention_head_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"generating inputs for {w.name}")
+    t0 = time.perf_counter()
+    x = workloads.make_inputs(w)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    head = gpu_case(tsa, torch, timer, w, x, args, args.stage_reps, args.steps, args.warmup, not args.no_dense)
+    log(f"{w.name}: {head['ms_per_step']:.3f} ms/step, stages {json.dumps(head['stage_ms'])}")
+    sweep = [head]
+    if not args.no_sweep and w.name.startswith("bf16_L128k"):
+        for name in ("bf16_L128k_r0.5", "bf16_L128k_r0.25", "bf16_L128k_r0.1"):
+            if name == w.name:
+                continue
+            wi = workloads.WORKLOADS[name]
+            res = gpu_case(tsa, torch, timer, wi, x, args, args.stage_reps, max(3, args.steps // 2), 1, False)
+            if "dense_ms" in head:
+                res["dense_ms"] = head["dense_ms"]
+                res["speedup_vs_dense"] = head["dense_ms"] / res["ms_per_step"]
+                res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
+            log(f"{wi.name}: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
+            sweep.append(res)
+
+    a = algorithmic(w)
+    attn_ms = head["stage_ms"]["attn"]
+    achieved = a["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": None, "kernel": "attn_kernel (tsa_attn)", "avg_launch_ms": attn_ms,
+                "algorithmic_per_launch": f"2*B*H*d*keep*(keep+1) = {a['attn_flops']:.4e} flop"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu = cpu_baseline(w, x)
+
+    line = {
+        "metric": "token-sparse attention prefill tokens/s + speedup vs dense at L=128K, bf16",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), bf16-rounded)",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "H": w.H, "Hkv": w.Hkv, "d": w.d, "keep": w.keep,
+                   "W": w.W, "n_sink": w.n_sink, "parallelism": "single GPU"},
+        "speedup_vs_dense": head.get("speedup_vs_dense"), "dense_ms": head.get("dense_ms"),
+        "stage_ms": head["stage_ms"], "stage_rate": head["stage_rate"],
+        "sweep": [{k: v for k, v in s.items() if k not in ("stage_rate",)} | {"stage_rate": s["stage_rate"]}
+                  for s in sweep],
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,8 +11,10 @@
 //   o_t = sum_{u <= t} softmax_u(scale <q_t, k_u>) v_u,   fp32 accumulation, one rounding.
 //
 // Design for gfx950 (CDNA4):
-// * A workgroup is 4 waves over BM = 4 * QB * 32 query rows of one (batch, head); each
-//   wave keeps its QB blocks of 32 query rows in registers as MFMA operands.
+// * A workgroup is NW waves over BM = NW * QB * 32 query rows of one (batch, head); each
+//   wave keeps its QB blocks of 32 query rows in registers as MFMA operands.  The bf16
+//   kernel runs 8 waves (2 per SIMD) within 256 registers each, so one wave's softmax
+//   arithmetic issues while the other wave's matrix instructions run.
 // * Key/value tiles of 64 rows stream through LDS, double buffered, with the next
 //   tile's global loads in flight while the current tile is on the matrix cores.
 // * Scores are formed transposed, S^T = K Q^T (32x32x16 bf16 MFMA), so a lane owns one
@@ -50,7 +52,6 @@ struct AttnParams {
   float c;                 // logit scale * log2(e)
 };
 
-constexpr int ATT_WAVES = 4;
 constexpr int BN = 64;          // keys per tile
 constexpr int KB = BN / 32;     // 32-key blocks per tile
 constexpr float NEG_BIG = -3.0e38f;
@@ -115,33 +116,33 @@ __device__ __forceinline__ void lds_k_frag<float, 128>(const float* ks, int key,
 
 // ---- global -> register -> LDS staging of one key/value tile --------------------------
 
-template <typename T, int D> struct Stage;
+template <typename T, int D, int NT> struct Stage;
 
-template <int D> struct Stage<__bf16, D> {
+template <int D, int NT> struct Stage<__bf16, D, NT> {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int KCH = BN * CPR / 256;         // K chunks per thread
-  static constexpr int VPAIRS = (BN / 4) * CPR;      // (4-key group, chunk) pairs
-  static constexpr int VPT = (VPAIRS + 255) / 256;   // pairs per thread
+  static constexpr int KCH = BN * CPR / NT;          // K chunks per thread
+  static constexpr int VUNITS = (BN / 2) * CPR;      // (2-key pair, chunk) units of V
+  static constexpr int VPT = (VUNITS + NT - 1) / NT; // V units per thread
   u32x4 kr[KCH];
-  u32x4 vr[VPT][4];
+  u32x4 vr[VPT][2];
 
   __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, int64_t rstride, int k0, int n,
                                        int tid) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int e = tid + 256 * i;
+      const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
       const int j = k0 + key;
       kr[i] = j < n ? ld16(kbase + (int64_t)j * rstride + c * 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int pr = tid + 256 * i;
-      if (pr < VPAIRS) {
-        const int a = pr / CPR, c = pr % CPR;
+      const int un = tid + NT * i;
+      if (VUNITS % NT == 0 || un < VUNITS) {
+        const int a = un / CPR, c = un % CPR;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = k0 + 4 * a + u;
+        for (int u = 0; u < 2; ++u) {
+          const int j = k0 + 2 * a + u;
           vr[i][u] = j < n ? ld16(vbase + (int64_t)j * rstride + c * 8) : u32x4{0, 0, 0, 0};
         }
       }
@@ -151,35 +152,34 @@ template <int D> struct Stage<__bf16, D> {
   __device__ __forceinline__ void store(AttnLds<__bf16, D>& L, int buf, int tid) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int e = tid + 256 * i;
+      const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
       *reinterpret_cast<u32x4*>(&L.k[buf][key * D + ((c ^ (key & 7)) << 3)]) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int pr = tid + 256 * i;
-      if (pr < VPAIRS) {
-        const int a = pr / CPR, c = pr % CPR;
-        const int pos = vt_pos(4 * a);                 // keys 4a..4a+3 occupy pos..pos+3
+      const int un = tid + NT * i;
+      if (VUNITS % NT == 0 || un < VUNITS) {
+        const int a = un / CPR, c = un % CPR;
+        const int pos = vt_pos(2 * a);                 // keys 2a, 2a+1 occupy pos, pos+1
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
           const int d = c * 8 + dd;
-          const int sh = (dd & 1) * 16;
-          const uint32_t e0 = (vr[i][0][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e1 = (vr[i][1][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e2 = (vr[i][2][dd >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e3 = (vr[i][3][dd >> 1] >> sh) & 0xFFFFu;
+          const uint32_t w0 = vr[i][0][dd >> 1], w1 = vr[i][1][dd >> 1];
+          // low halves (even dd) or high halves (odd dd) of the two keys, packed
+          const uint32_t packed = (dd & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                                           : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
           const int off = d * BN + ((((pos >> 3) ^ vt_swz(d))) << 3) + (pos & 7);
-          *reinterpret_cast<u32x2*>(&L.vt[buf][off]) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+          *reinterpret_cast<uint32_t*>(&L.vt[buf][off]) = packed;
         }
       }
     }
   }
 };
 
-template <int D> struct Stage<float, D> {
+template <int D, int NT> struct Stage<float, D, NT> {
   static constexpr int CPR = D / 4;
-  static constexpr int CH = BN * CPR / 256;
+  static constexpr int CH = BN * CPR / NT;
   u32x4 kr[CH];
   u32x4 vr[CH];
 
@@ -187,7 +187,7 @@ template <int D> struct Stage<float, D> {
                                        int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int e = tid + 256 * i;
+      const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
       const int j = k0 + key;
       kr[i] = j < n ? ld16(kbase + (int64_t)j * rstride + c * 4) : u32x4{0, 0, 0, 0};
@@ -198,7 +198,7 @@ template <int D> struct Stage<float, D> {
   __device__ __forceinline__ void store(AttnLds<float, D>& L, int buf, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int e = tid + 256 * i;
+      const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
       *reinterpret_cast<u32x4*>(&L.k[buf][key * D + ((c ^ (key & 7)) << 2)]) = kr[i];
       *reinterpret_cast<u32x4*>(&L.v[buf][key * D + c * 4]) = vr[i];
@@ -264,10 +264,10 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
-template <typename T, int D, int QB>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+template <typename T, int D, int QB, int NW>
+__global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
   __shared__ AttnLds<T, D> lds;
-  constexpr int BM = ATT_WAVES * QB * 32;
+  constexpr int BM = NW * QB * 32;
   const int tid = threadIdx.x;
   const int wave = tid / TSA_WAVE;
   const int lane = lane_id();
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     for (int db = 0; db < D / 32; ++db) o[qb][db] = f32x16{};
   }
 
-  Stage<T, D> st;
+  Stage<T, D, NW * TSA_WAVE> st;
   st.load(kbase, vbase, p.k_r, 0, p.n, tid);
   for (int t = 0; t < nkt; ++t) {
     const int buf = t & 1;
@@ -398,23 +398,23 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   }
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D, int QB, int NW>
 hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
-  constexpr int BM = ATT_WAVES * QB * 32;
+  constexpr int BM = NW * QB * 32;
   p.BH = B * H;
   p.ntiles = (p.n + BM - 1) / BM;
   const int64_t blocks = (int64_t)p.BH * p.ntiles;
-  attn_kernel<T, D, QB><<<(unsigned)blocks, 256, 0, s>>>(p);
+  attn_kernel<T, D, QB, NW><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t dispatch_attn(const tsa_desc& d, AttnParams p, hipStream_t s) {
   if (d.dtype == TSA_BF16) {
-    if (d.d == 128) return launch_attn_t<__bf16, 128, 1>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_t<__bf16, 64, 2>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_t<__bf16, 128, 1, 8>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_t<__bf16, 64, 1, 8>(p, d.B, d.H, s);
   } else {
-    if (d.d == 128) return launch_attn_t<float, 128, 1>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_t<float, 64, 1>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_t<float, 128, 1, 4>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_t<float, 64, 1, 4>(p, d.B, d.H, s);
   }
   return hipErrorInvalidValue;
 }
