@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--stage-reps", type=int, default=5)
+    p.add_argument("--stage", choices=["score", "select", "gather", "attn", "scatter", "dense", "forward", "copy"],
+                   help="run only this stage (after one full forward to make its inputs) --stage-reps times; "
+                        "for profiler runs")
     return p.parse_args()
 
 
@@ -62,6 +65,29 @@ class Timer:
         b.record(s)
         t.cuda.synchronize()
         return a.elapsed_time(b) / reps
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_L128k_r0.5_hbm_traffic.txt")
+ATTN_SOURCES = ["token_sparse_attention_head_amd/csrc/attn.hip", "token_sparse_attention_head_amd/csrc/common.h"]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when it was taken on another workload or another attention source."""
+    import hashlib
+    if workload != "bf16_L128k_r0.5" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.split()[0] if v.split() else ""
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "hbm_bytes_per_launch" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
 
 
 def algorithmic(w):
@@ -144,6 +170,41 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense):
     return res
 
 
+def stage_only(tsa, torch, timer, w, x, name, reps):
+    """One forward to build the stage inputs, then only `name`, reps times.  `copy` is a
+    plain 1 GiB device-to-device copy (torch), the reference for HBM byte counters."""
+    if name == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        ms = timer.run(lambda: dst.copy_(src), reps)
+        return {"stage": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "reps": reps, "avg_ms": ms}
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
+    desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink)
+    B, L, H, D = q.shape
+    scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    idx = torch.empty(B, H, w.keep, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(r)
+    ws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
+    sws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCORE)), dtype=torch.uint8, device="cuda")
+    cws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCATTER)), dtype=torch.uint8, device="cuda")
+    tsa.tsa_forward(desc, q, k, v, r, out, scores, idx, ws)
+    comp = [torch.empty(B, H, w.keep, D, dtype=dt, device="cuda") for _ in range(4)]
+    tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2])
+    o = torch.empty_like(q) if name == "dense" else None
+    fns = {
+        "score": lambda: tsa.tsa_score(desc, q, k, scores, sws),
+        "select": lambda: tsa.tsa_select(desc, scores, idx),
+        "gather": lambda: tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2]),
+        "attn": lambda: tsa.tsa_attn(desc, comp[0], comp[1], comp[2], comp[3]),
+        "scatter": lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r, out, cws),
+        "dense": lambda: tsa.tsa_dense_attn(desc, q, k, v, o),
+        "forward": lambda: tsa.tsa_forward(desc, q, k, v, r, out, None, None, ws),
+    }
+    ms = timer.run(fns[name], reps)
+    return {"workload": w.name, "stage": name, "reps": reps, "avg_ms": ms}
+
+
 def cpu_baseline(w, x, budget_s=20.0):
     """Time the float64 oracle on a bounded sample of the workload: one (batch, head)'s
     scores, subset, gather and scatter in full, and compact attention rows sampled evenly
@@ -214,6 +275,9 @@ def main():
     x = workloads.make_inputs(w)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
 
+    if args.stage:
+        print(json.dumps(stage_only(tsa, torch, timer, w, x, args.stage, args.stage_reps)), flush=True)
+        return
     head = gpu_case(tsa, torch, timer, w, x, args, args.stage_reps, args.steps, args.warmup, not args.no_dense)
     log(f"{w.name}: {head['ms_per_step']:.3f} ms/step, stages {json.dumps(head['stage_ms'])}")
     sweep = [head]
@@ -235,7 +299,8 @@ def main():
     achieved = a["attn_flops"] / (attn_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": None, "kernel": "attn_kernel (tsa_attn)", "avg_launch_ms": attn_ms,
+                "traffic": measured_traffic(w.name), "traffic_unit": "HBM bytes per launch",
+                "kernel": "attn_kernel (tsa_attn)", "avg_launch_ms": attn_ms,
                 "algorithmic_per_launch": f"2*B*H*d*keep*(keep+1) = {a['attn_flops']:.4e} flop"}
     cpu = None
     if not args.no_cpu_baseline:

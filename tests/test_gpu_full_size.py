@@ -1,0 +1,125 @@
+"""Parity at the full workload sizes, through tsa_forward as bench.py calls it.
+
+The oracle cannot redo a whole 131072-token layer in seconds, so each case checks what
+it can compute one by one: the scores, subset and attention rows of a sample of heads
+(exact oracle arithmetic on those heads), and, over the whole tensor, the properties
+that hold at any size (unselected rows equal the residual bit for bit; every subset has
+keep ascending positions including the forced ones).  The planted-importance workload
+also checks that every head of a KV group keeps that group's planted keys and that the
+heads' subsets differ."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._lib import ensure_built
+from tests.gpu_helpers import TOL, check_selection, half_ulp, rel_err
+
+pytestmark = pytest.mark.gpu
+
+tsa = ensure_built()
+
+_CACHE = {}
+
+
+def _inputs(name):
+    w = workloads.WORKLOADS[name]
+    key = (w.B, w.L, w.H, w.Hkv, w.d, w.dtype, w.planted, w.seed)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = workloads.make_inputs(w)
+    return w, _CACHE[key]
+
+
+def _run(w, x):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
+    out, sg, ig = tsa.forward(q, k, v, r, w.keep, w.W, w.n_sink, return_scores=True)
+    torch.cuda.synchronize()
+    return q, k, v, r, out, sg, ig
+
+
+def _check(w, x, heads, rows_per_head=12, seed=0):
+    q, k, v, r, out, sg, ig = _run(w, x)
+    B, L, H, d = x["q"].shape
+    G = H // w.Hkv
+    scale = 1.0 / np.sqrt(d)
+
+    # Whole-tensor properties.
+    idx_all = ig.cpu().numpy().astype(np.int64)
+    assert idx_all.shape == (B, H, w.keep)
+    assert np.all(np.diff(idx_all, axis=-1) > 0)
+    F = oracle.forced_positions(L, w.W, w.n_sink)
+    assert np.all(np.isin(F, idx_all[0, 0])) and np.all(np.isin(F, idx_all[-1, -1]))
+    sel = torch.zeros(B, H, L, dtype=torch.bool, device="cuda")
+    sel.scatter_(2, ig.long(), True)
+    sel = sel.permute(0, 2, 1)                                  # [B, L, H]
+    assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16))
+    assert int(sel.sum()) == B * H * w.keep
+
+    rng = np.random.default_rng(seed)
+    s_gpu_all = sg.cpu().numpy().astype(np.float64)
+    worst_s, worst_out, n_diff = 0.0, 0.0, 0
+    for b, h in heads:
+        g = h // G
+        qh = x["q"][b, :, h, :].astype(np.float64)
+        kg = x["k"][b, :, g, :].astype(np.float64)
+        vg = x["v"][b, :, g, :].astype(np.float64)
+        s_or = oracle.score_head(qh, kg, w.W, scale)
+        s_gpu = s_gpu_all[b, h]
+        worst_s = max(worst_s, rel_err(s_gpu, s_or))
+        idx = idx_all[b, h]
+        assert np.array_equal(idx, oracle.select_row(s_gpu, w.keep, w.W, w.n_sink))   # select bit-exact
+        n_diff += check_selection(s_or[None, None], idx[None, None], w.keep, w.W, w.n_sink)
+        # Attention rows on the GPU's subset: first, last and random compact rows.
+        rows = np.unique(np.concatenate([[0, w.keep - 1], rng.integers(0, w.keep, rows_per_head)]))
+        o_rows = oracle.attend_rows(qh[idx], kg[idx], vg[idx], rows, scale)
+        pos = idx[rows]
+        got = out[b, torch.from_numpy(pos).cuda(), h, :].float().cpu().numpy().astype(np.float64)
+        want = x["r"][b, pos, h, :].astype(np.float64) + o_rows
+        excess = np.abs(got - want) - half_ulp(got, w.dtype)
+        worst_out = max(worst_out, float(excess.max()))
+    print(f"{w.name}: score rel err {worst_s:.2e}, out excess {worst_out:.2e}, subset differences {n_diff}")
+    assert worst_s <= 1e-5
+    assert worst_out <= TOL[w.dtype]
+    return idx_all
+
+
+def test_full_bf16_L8k_r05():
+    w, x = _inputs("bf16_L8k_r0.5")
+    _check(w, x, heads=[(0, 0), (0, 5), (0, 13), (0, 31)])
+
+
+def test_full_bf16_L32k_r025():
+    w, x = _inputs("bf16_L32k_r0.25")
+    _check(w, x, heads=[(0, 2), (0, 19)])
+
+
+@pytest.mark.parametrize("name", ["bf16_L128k_r0.1", "bf16_L128k_r0.5"])
+def test_full_bf16_L128k(name):
+    w, x = _inputs(name)
+    _check(w, x, heads=[(0, 0), (0, 30)], rows_per_head=8)
+
+
+def test_full_planted_recall_and_distinct_heads():
+    w, x = _inputs("bf16_L64k_planted")
+    idx = _check(w, x, heads=[(0, 1), (1, 22)], rows_per_head=8)
+    G = w.G
+    recalls, jac = [], []
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            P = x["planted"][(b, g)]
+            sets = []
+            for h in range(g * G, (g + 1) * G):
+                S = idx[b, h]
+                recalls.append(np.isin(P, S).mean())
+                sets.append(set(S.tolist()))
+            for i in range(G):
+                for j in range(i + 1, G):
+                    assert sets[i] != sets[j]
+                    jac.append(len(sets[i] & sets[j]) / len(sets[i] | sets[j]))
+    print(f"planted recall min {min(recalls):.4f} mean {np.mean(recalls):.4f}; within-group Jaccard mean "
+          f"{np.mean(jac):.3f} max {max(jac):.3f}")
+    assert min(recalls) >= 0.99
+    assert max(jac) < 0.5

@@ -115,6 +115,8 @@ __device__ __forceinline__ void lds_k_frag<float, 128>(const float* ks, int key,
 }
 
 // ---- global -> register -> LDS staging of one key/value tile --------------------------
+// Rows past the end of the sequence are loaded as copies of the last row: they only
+// meet queries that mask them (probability exactly 0), so any finite value will do.
 
 template <typename T, int D, int NT> struct Stage;
 
@@ -132,8 +134,8 @@ template <int D, int NT> struct Stage<__bf16, D, NT> {
     for (int i = 0; i < KCH; ++i) {
       const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
-      const int j = k0 + key;
-      kr[i] = j < n ? ld16(kbase + (int64_t)j * rstride + c * 8) : u32x4{0, 0, 0, 0};
+      const int j = min(k0 + key, n - 1);
+      kr[i] = ld16(kbase + (int64_t)j * rstride + c * 8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -142,8 +144,8 @@ template <int D, int NT> struct Stage<__bf16, D, NT> {
         const int a = un / CPR, c = un % CPR;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int j = k0 + 2 * a + u;
-          vr[i][u] = j < n ? ld16(vbase + (int64_t)j * rstride + c * 8) : u32x4{0, 0, 0, 0};
+          const int j = min(k0 + 2 * a + u, n - 1);
+          vr[i][u] = ld16(vbase + (int64_t)j * rstride + c * 8);
         }
       }
     }
@@ -189,9 +191,9 @@ template <int D, int NT> struct Stage<float, D, NT> {
     for (int i = 0; i < CH; ++i) {
       const int e = tid + NT * i;
       const int key = e / CPR, c = e % CPR;
-      const int j = k0 + key;
-      kr[i] = j < n ? ld16(kbase + (int64_t)j * rstride + c * 4) : u32x4{0, 0, 0, 0};
-      vr[i] = j < n ? ld16(vbase + (int64_t)j * rstride + c * 4) : u32x4{0, 0, 0, 0};
+      const int j = min(k0 + key, n - 1);
+      kr[i] = ld16(kbase + (int64_t)j * rstride + c * 4);
+      vr[i] = ld16(vbase + (int64_t)j * rstride + c * 4);
     }
   }
 
@@ -256,6 +258,47 @@ __device__ __forceinline__ void pv_tile(const AttnLds<float, D>& L, int buf, int
       }
 }
 
+// Online softmax of one tile for the wave's query blocks: masks keys above the diagonal
+// (only on tiles that reach it), moves the running max lazily, turns scores into
+// probabilities in place and accumulates the lane's share of the row sums.
+template <bool MASK, int QB, int ND>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB][QB], float (&m)[QB], float (&l)[QB],
+                                             f32x16 (&o)[QB][ND], int k0, int wrow0, int hf, int lc, float c) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    // key k0 + kb*32 + acc_row(r, hf) is above the diagonal iff acc_row(r, 0) > lim - 32*kb
+    const int lim = wrow0 + qb * 32 + lc - k0 - 4 * hf;
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MASK && acc_row(r, 0) > lim - 32 * kb) s[kb][qb][r] = -__builtin_huge_valf();
+        tmax = fmaxf(tmax, s[kb][qb][r]);
+      }
+    tmax = fmaxf(tmax, xor32(tmax));
+    const float mt = tmax * c;
+    if (__ballot(mt > m[qb] + RESCALE_SLACK) != 0) {
+      const float mn = fmaxf(m[qb], mt);
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+      l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[qb][db] *= alpha;
+      m[qb] = mn;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
+        s[kb][qb][r] = pr;
+        lsum += pr;
+      }
+    l[qb] += lsum;
+  }
+}
+
 template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
@@ -264,8 +307,15 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
-template <typename T, int D, int QB, int NW>
+// DENSE selects the strided [B][L][H][d] layout with grouped KV heads (the library's dense
+// reference); otherwise rows are the contiguous compact [B][H][keep][d] tensors and the
+// row strides are compile-time constants.
+template <typename T, int D, int QB, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
+  if (!DENSE) {
+    p.q_r = p.k_r = p.o_r = D;
+    p.kv_div = 1;
+  }
   __shared__ AttnLds<T, D> lds;
   constexpr int BM = NW * QB * 32;
   const int tid = threadIdx.x;
@@ -342,39 +392,10 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
       }
     }
 
-    const bool need_mask = k0 + BN - 1 > wrow0;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int i = wrow0 + qb * 32 + lc;
-      float tmax = -__builtin_huge_valf();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (need_mask && k0 + kb * 32 + acc_row(r, hf) > i) s[kb][qb][r] = -__builtin_huge_valf();
-          tmax = fmaxf(tmax, s[kb][qb][r]);
-        }
-      tmax = fmaxf(tmax, xor32(tmax));
-      const float mt = tmax * p.c;
-      if (__ballot(mt > m[qb] + RESCALE_SLACK) != 0) {
-        const float mn = fmaxf(m[qb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha;
-        m[qb] = mn;
-      }
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.c, -m[qb]));
-          s[kb][qb][r] = pr;
-          lsum += pr;
-        }
-      l[qb] += lsum;
-    }
+    if (k0 + BN - 1 > wrow0)
+      softmax_tile<true, QB>(s, m, l, o, k0, wrow0, hf, lc, p.c);
+    else
+      softmax_tile<false, QB>(s, m, l, o, k0, wrow0, hf, lc, p.c);
 
     pv_tile<D, QB>(lds, buf, lane, s, o);
   }
@@ -398,23 +419,24 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
   }
 }
 
-template <typename T, int D, int QB, int NW>
+template <typename T, int D, int QB, int NW, bool DENSE>
 hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW * QB * 32;
   p.BH = B * H;
   p.ntiles = (p.n + BM - 1) / BM;
   const int64_t blocks = (int64_t)p.BH * p.ntiles;
-  attn_kernel<T, D, QB, NW><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
+  attn_kernel<T, D, QB, NW, DENSE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
 }
 
+template <bool DENSE>
 hipError_t dispatch_attn(const tsa_desc& d, AttnParams p, hipStream_t s) {
   if (d.dtype == TSA_BF16) {
-    if (d.d == 128) return launch_attn_t<__bf16, 128, 1, 8>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_t<__bf16, 64, 1, 8>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_t<__bf16, 128, 1, 8, DENSE>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_t<__bf16, 64, 1, 8, DENSE>(p, d.B, d.H, s);
   } else {
-    if (d.d == 128) return launch_attn_t<float, 128, 1, 4>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_t<float, 64, 1, 4>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_t<float, 128, 1, 4, DENSE>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_t<float, 64, 1, 4, DENSE>(p, d.B, d.H, s);
   }
   return hipErrorInvalidValue;
 }
@@ -437,7 +459,7 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
   p.k_r = p.q_r; p.k_h = p.q_h; p.k_b = p.q_b;
   p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
   p.c = attn_c(d);
-  return dispatch_attn(d, p, s);
+  return dispatch_attn<false>(d, p, s);
 }
 
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
@@ -451,7 +473,7 @@ hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, co
   p.k_r = (int64_t)d.Hkv * d.d; p.k_h = d.d; p.k_b = (int64_t)d.L * d.Hkv * d.d;
   p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
   p.c = attn_c(d);
-  return dispatch_attn(d, p, s);
+  return dispatch_attn<true>(d, p, s);
 }
 
 }  // namespace tsa
