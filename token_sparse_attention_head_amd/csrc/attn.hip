@@ -58,44 +58,14 @@ constexpr float NEG_BIG = -3.0e38f;
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units
 
 template <typename T, int D> struct AttnLds;
-template <int D> struct AttnLds<__bf16, D> {
-  __bf16 k[2][BN * D];    // [key][d], 16-byte chunks swizzled by key
-  __bf16 vt[2][D * BN];   // [d][permuted key], 16-byte chunks swizzled by d
-};
 template <int D> struct AttnLds<float, D> {
   float k[2][BN * D];     // [key][d], 16-byte chunks swizzled by key
   float v[2][BN * D];     // [key][d]
 };
 
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
-// Position of tile key w in the transposed V layout: inside each 16-key group, keys
-// {0-3, 8-11} take slots 0-7 and keys {4-7, 12-15} take slots 8-15, which is the order
-// in which the two lane halves hold probabilities of that group.
-__device__ __forceinline__ int vt_pos(int w) {
-  const int w16 = w & 15;
-  return (w & ~15) + 8 * ((w16 & 7) >> 2) + 4 * (w16 >> 3) + (w16 & 3);
-}
-
 template <typename T, int D>
 __device__ __forceinline__ void lds_k_frag(const T* ks, int key, int hf, HalfRow<T, D>& f);
 
-template <>
-__device__ __forceinline__ void lds_k_frag<__bf16, 128>(const __bf16* ks, int key, int hf, HalfRow<__bf16, 128>& f) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int c = hf * 8 + s;
-    f.f[s] = *reinterpret_cast<const bf16x8*>(ks + key * 128 + ((c ^ (key & 7)) << 3));
-  }
-}
-template <>
-__device__ __forceinline__ void lds_k_frag<__bf16, 64>(const __bf16* ks, int key, int hf, HalfRow<__bf16, 64>& f) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = hf * 4 + s;
-    f.f[s] = *reinterpret_cast<const bf16x8*>(ks + key * 64 + ((c ^ (key & 7)) << 3));
-  }
-}
 template <int D>
 __device__ __forceinline__ void lds_k_frag_f32(const float* ks, int key, int hf, HalfRow<float, D>& f) {
 #pragma unroll
@@ -119,65 +89,6 @@ __device__ __forceinline__ void lds_k_frag<float, 128>(const float* ks, int key,
 // meet queries that mask them (probability exactly 0), so any finite value will do.
 
 template <typename T, int D, int NT> struct Stage;
-
-template <int D, int NT> struct Stage<__bf16, D, NT> {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int KCH = BN * CPR / NT;          // K chunks per thread
-  static constexpr int VUNITS = (BN / 2) * CPR;      // (2-key pair, chunk) units of V
-  static constexpr int VPT = (VUNITS + NT - 1) / NT; // V units per thread
-  u32x4 kr[KCH];
-  u32x4 vr[VPT][2];
-
-  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, int64_t rstride, int k0, int n,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int e = tid + NT * i;
-      const int key = e / CPR, c = e % CPR;
-      const int j = min(k0 + key, n - 1);
-      kr[i] = ld16(kbase + (int64_t)j * rstride + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int un = tid + NT * i;
-      if (VUNITS % NT == 0 || un < VUNITS) {
-        const int a = un / CPR, c = un % CPR;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = min(k0 + 2 * a + u, n - 1);
-          vr[i][u] = ld16(vbase + (int64_t)j * rstride + c * 8);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(AttnLds<__bf16, D>& L, int buf, int tid) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int e = tid + NT * i;
-      const int key = e / CPR, c = e % CPR;
-      *reinterpret_cast<u32x4*>(&L.k[buf][key * D + ((c ^ (key & 7)) << 3)]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int un = tid + NT * i;
-      if (VUNITS % NT == 0 || un < VUNITS) {
-        const int a = un / CPR, c = un % CPR;
-        const int pos = vt_pos(2 * a);                 // keys 2a, 2a+1 occupy pos, pos+1
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int d = c * 8 + dd;
-          const uint32_t w0 = vr[i][0][dd >> 1], w1 = vr[i][1][dd >> 1];
-          // low halves (even dd) or high halves (odd dd) of the two keys, packed
-          const uint32_t packed = (dd & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                           : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-          const int off = d * BN + ((((pos >> 3) ^ vt_swz(d))) << 3) + (pos & 7);
-          *reinterpret_cast<uint32_t*>(&L.vt[buf][off]) = packed;
-        }
-      }
-    }
-  }
-};
 
 template <int D, int NT> struct Stage<float, D, NT> {
   static constexpr int CPR = D / 4;
@@ -209,37 +120,6 @@ template <int D, int NT> struct Stage<float, D, NT> {
 };
 
 // ---- P.V for one tile -----------------------------------------------------------------
-
-template <int D, int QB>
-__device__ __forceinline__ void pv_tile(const AttnLds<__bf16, D>& L, int buf, int lane,
-                                        const f32x16 (&s)[KB][QB], f32x16 (&o)[QB][D / 32]) {
-  const int hf = lane >> 5, lc = lane & 31;
-  // Probabilities as bf16 B operands: k-step (kb, jj) uses accumulator slots 8jj..8jj+7.
-  bf16x8 pf[QB][KB][2];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pf[qb][kb][jj][u] = static_cast<__bf16>(s[kb][qb][8 * jj + u]);
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int d = db * 32 + lc;
-    const __bf16* row = &L.vt[buf][d * BN];
-    const int sw = vt_swz(d);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int chunk = 2 * (2 * kb + jj) + hf;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(row + ((chunk ^ sw) << 3));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma(o[qb][db], vf, pf[qb][kb][jj]);
-      }
-  }
-}
 
 template <int D, int QB>
 __device__ __forceinline__ void pv_tile(const AttnLds<float, D>& L, int buf, int lane,
@@ -419,6 +299,253 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
   }
 }
 
+// ---- bf16 kernel ------------------------------------------------------------------------
+//
+// Same dataflow as attn_kernel, with the gfx950 transposing LDS read for the P.V operand:
+// ds_read_b64_tr_b16 hands lane i of each 16-lane block element i % 4 of the 8 bytes that
+// lanes 4j + i/4 (j = 0..3) address.  Pointing lane s at V[k0 + s/4][d0 + 4 (s%4) .. +3]
+// of a row-major [key][d] tile therefore gives lane i the values V[k0 + j][d0 + i]: the
+// V^T operand, read straight from the natural layout.  K and V tiles are both stored as
+// loaded (one 16-byte store per chunk, no shuffling).  Rows are padded instead of
+// swizzled, so every operand address is one register plus an immediate: K rows are
+// 2d+16 bytes apart (consecutive keys move 4 banks, so the 16 rows one read cycle touches
+// cover every bank once), V rows 2d+32 apart (the four key rows of a transposing read sit
+// on disjoint 8-bank ranges).  The tile loop is unrolled by two so the buffer offsets are
+// immediates too, and the row pointers of the global loads advance by one add per tile.
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 tr_read2(const char* a, const char* b) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)b);
+  const i16x8 z = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Value of the other 32-lane half (lane l ^ 32) in one VALU instruction: v_permlane32_swap
+// of a register pair returns {lo, lo} and {hi, hi}.
+__device__ __forceinline__ float half_swap(float x) {
+  const u32x2 pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(__lane_id() < 32 ? pr[1] : pr[0]);
+}
+
+template <int D, int NW, bool DENSE>
+__global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) {
+  constexpr int NT = NW * TSA_WAVE;
+  constexpr int BM = NW * 32;
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int LOADS = BN * CPR / NT;            // chunks per lane per tensor per tile
+  static_assert(LOADS >= 1 && BN * CPR % NT == 0, "a tile splits evenly over the lanes");
+  constexpr int KP = 2 * D + 16, VP = 2 * D + 32; // padded row pitches, bytes
+  struct Buf {
+    char k[BN * KP];
+    char v[BN * VP];
+  };
+  __shared__ __attribute__((aligned(16))) Buf lds[2];
+
+  // Arguments in registers (lambdas capture by reference; a captured argument struct
+  // would be placed in scratch memory).
+  const int n = p.n;
+  const int64_t q_r = DENSE ? p.q_r : D, k_r = DENSE ? p.k_r : D, o_r = DENSE ? p.o_r : D;
+  const int kv_div = DENSE ? p.kv_div : 1;
+  const float c = p.c;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / TSA_WAVE;
+  const int lane = lane_id();
+  const int hf = lane >> 5, lc = lane & 31;
+
+  int bh, tile;
+  {
+    const int bid = blockIdx.x;
+    if (p.BH % 8 == 0) {
+      const int hpx = p.BH / 8;
+      const int x = bid % 8, sl = bid / 8;
+      bh = x * hpx + sl % hpx;
+      tile = p.ntiles - 1 - sl / hpx;
+    } else {
+      bh = bid % p.BH;
+      tile = p.ntiles - 1 - bid / p.BH;
+    }
+  }
+  const int64_t b = bh / p.H;
+  const int h = bh % p.H;
+  const int kvh = h / kv_div;
+  const __bf16* qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_b + h * p.q_h;
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h;
+  __bf16* obase = reinterpret_cast<__bf16*>(p.o) + b * p.o_b + h * p.o_h;
+
+  const int q0 = tile * BM;
+  const int wrow0 = q0 + wave * 32;
+  const int wave_last = min(n - 1, wrow0 + 31);
+  const int nkt = (min(n, q0 + BM) - 1) / BN + 1;
+
+  // Staging: chunk i of this lane is row lrow[i], chunk lchunk[i] of the tile.
+  int lrow[LOADS], soff_k[LOADS], soff_v[LOADS];
+  const __bf16* kptr[LOADS];
+  const __bf16* vptr[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int e = tid + NT * i;
+    const int ch = e % CPR;
+    lrow[i] = e / CPR;
+    soff_k[i] = lrow[i] * KP + ch * 16;
+    soff_v[i] = lrow[i] * VP + ch * 16;
+    kptr[i] = kbase + (int64_t)lrow[i] * k_r + ch * 8;
+    vptr[i] = vbase + (int64_t)lrow[i] * k_r + ch * 8;
+  }
+  u32x4 kst[LOADS], vst[LOADS];
+  int next_k0 = 0;
+  // Loads the next tile into registers; rows past the end repeat the last row (they
+  // only meet queries that mask them).
+  auto load_next = [&]() __attribute__((always_inline)) {
+    if (next_k0 + BN <= n) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        kst[i] = ld16(kptr[i]);
+        vst[i] = ld16(vptr[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t back = (int64_t)(max(next_k0 + lrow[i] - (n - 1), 0)) * k_r;
+        kst[i] = ld16(kptr[i] - back);
+        vst[i] = ld16(vptr[i] - back);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      kptr[i] += BN * k_r;
+      vptr[i] += BN * k_r;
+    }
+    next_k0 += BN;
+  };
+
+  HalfRow<__bf16, D> qf;
+  {
+    const int row = wrow0 + lc;
+    if (row < n)
+      qf.load(qbase + (int64_t)row * q_r + hf * (D / 2));
+    else
+      qf.zero();
+  }
+  const int koff = lc * KP + hf * D;                   // QK operand: key lc, d from hf * D/2
+  const int blk = lane >> 4, sl = lane & 15;
+  const int voff = (4 * (blk >> 1) + (sl >> 2)) * VP + (16 * (blk & 1) + 4 * (sl & 3)) * 2;
+
+  f32x16 o[D / 32];
+  float m = NEG_BIG, l = 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+
+  auto step = [&](int t, Buf& cur) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      *reinterpret_cast<u32x4*>(cur.k + soff_k[i]) = kst[i];
+      *reinterpret_cast<u32x4*>(cur.v + soff_v[i]) = vst[i];
+    }
+    __syncthreads();
+    if (t + 1 < nkt) load_next();
+    const int k0 = t * BN;
+    if (wrow0 > wave_last || k0 > wave_last) return;   // no key of this tile is visible
+
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cur.k + kb * 32 * KP + koff + s2 * 16);
+        s[kb] = mfma(s[kb], kf, qf.f[s2]);
+      }
+    }
+
+    // Online softmax of the tile (mask only where the tile reaches the diagonal).
+    const bool diag = k0 + BN - 1 > wrow0;
+    const int lim = wrow0 + lc - k0 - 4 * hf;
+    float tmax = -__builtin_huge_valf();
+    if (diag) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (acc_row(r, 0) > lim - 32 * kb) s[kb][r] = -__builtin_huge_valf();
+          tmax = fmaxf(tmax, s[kb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+    }
+    tmax = fmaxf(tmax, half_swap(tmax));
+    const float mt = tmax * c;
+    if (__ballot(mt > m + RESCALE_SLACK) != 0) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      m = mn;
+    }
+    bf16x8 pf[KB][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m));
+        lsum += pr;
+        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(pr);
+      }
+    l += lsum;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const char* a = cur.v + (kb * 32 + 16 * jj) * VP + voff + db * 64;
+          o[db] = mfma(o[db], tr_read2(a, a + 8 * VP), pf[kb][jj]);
+        }
+  };
+
+  load_next();
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, lds[0]);
+    if (t + 1 < nkt) step(t + 1, lds[1]);
+  }
+
+  const float inv = 1.0f / (l + half_swap(l));
+  const int i = wrow0 + lc;
+  if (i < n) {
+    __bf16* orow = obase + (int64_t)i * o_r;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * hf;
+        store4<__bf16>(orow + d0, o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                       o[db][4 * r4 + 3] * inv);
+      }
+  }
+}
+
+template <int D, int NW, bool DENSE>
+hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
+  constexpr int BM = NW * 32;
+  p.BH = B * H;
+  p.ntiles = (p.n + BM - 1) / BM;
+  const int64_t blocks = (int64_t)p.BH * p.ntiles;
+  attn_bf16_kernel<D, NW, DENSE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int QB, int NW, bool DENSE>
 hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW * QB * 32;
@@ -432,8 +559,8 @@ hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
 template <bool DENSE>
 hipError_t dispatch_attn(const tsa_desc& d, AttnParams p, hipStream_t s) {
   if (d.dtype == TSA_BF16) {
-    if (d.d == 128) return launch_attn_t<__bf16, 128, 1, 8, DENSE>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_t<__bf16, 64, 1, 8, DENSE>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_bf16<128, 8, DENSE>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_bf16<64, 8, DENSE>(p, d.B, d.H, s);
   } else {
     if (d.d == 128) return launch_attn_t<float, 128, 1, 4, DENSE>(p, d.B, d.H, s);
     if (d.d == 64) return launch_attn_t<float, 64, 1, 4, DENSE>(p, d.B, d.H, s);
