@@ -309,8 +309,9 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
 // loaded (one 16-byte store per chunk, no shuffling).  Rows are padded instead of
 // swizzled, so every operand address is one register plus an immediate: K rows are
 // 2d+16 bytes apart (consecutive keys move 4 banks, so the 16 rows one read cycle touches
-// cover every bank once), V rows 2d+32 apart (the four key rows of a transposing read sit
-// on disjoint 8-bank ranges).  The tile loop is unrolled by two so the buffer offsets are
+// cover every bank once), V rows 2d+64 apart (a transposing read serves 32 lanes per
+// cycle from 64 banks: four key rows x two 16-lane blocks must fall on disjoint 8-bank
+// ranges, which needs rows 16 banks apart; measured conflict-free, 2d+32 is not).  The tile loop is unrolled by two so the buffer offsets are
 // immediates too, and the row pointers of the global loads advance by one add per tile.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / NT;            // chunks per lane per tensor per tile
   static_assert(LOADS >= 1 && BN * CPR % NT == 0, "a tile splits evenly over the lanes");
-  constexpr int KP = 2 * D + 16, VP = 2 * D + 32; // padded row pitches, bytes
+  constexpr int KP = 2 * D + 16, VP = 2 * D + 64; // padded row pitches, bytes
   struct Buf {
     char k[BN * KP];
     char v[BN * VP];
