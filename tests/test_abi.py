@@ -54,7 +54,11 @@ def test_workspace_sizes():
     assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) == 0
     assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SCATTER) == 32 * 8192 * 4
     fwd = tsa.tsa_workspace_size(d, tsa.TSA_OP_FORWARD)
-    assert fwd >= 4 * 32 * 4096 * 128 * 2 + 2 * 32 * 8192 * 4
+    # bf16 forward is fused: scores, idx and the inverse map, no compact tensors
+    assert 2 * 32 * 8192 * 4 + 32 * 4096 * 4 <= fwd < 4 * 32 * 4096 * 128 * 2
+    # fp32 forward runs the stages: four compact [B,H,keep,d] tensors as well
+    fwd32 = tsa.tsa_workspace_size(D(dtype=tsa.TSA_F32), tsa.TSA_OP_FORWARD)
+    assert fwd32 >= 4 * 32 * 4096 * 128 * 4 + 2 * 32 * 8192 * 4
     assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SCORE) > 0
     with pytest.raises(tsa.TsaError) as e:
         tsa.tsa_workspace_size(d, 17)

@@ -241,6 +241,25 @@ def test_hand_cases_through_gpu(case):
     assert np.all(host(out)[0, :, 0, 2:] == 0)
 
 
+@pytest.mark.parametrize("B,H,Hkv,L,d,keep,in_place", [(2, 8, 2, 1234, 128, 500, False), (1, 8, 2, 1234, 128, 500, True),
+                                                      (1, 4, 4, 999, 64, 300, False), (1, 4, 1, 3000, 128, 3000, False)])
+def test_fused_forward_equals_staged(B, H, Hkv, L, d, keep, in_place):
+    # The bf16 forward reads rows through the index lists and writes residual + O from the
+    # attention epilogue; it must equal the staged entry points (gather, attention on the
+    # compact rows, scatter + residual) bit for bit.
+    x = workloads.small_random(B, H, Hkv, L, d, seed=17, dtype="bf16")
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    if in_place:
+        out = r.clone()
+        _, s_f, idx = tsa.forward(q, k, v, out, keep, 64, 4, out=out, return_scores=True)
+    else:
+        out, s_f, idx = tsa.forward(q, k, v, r, keep, 64, 4, return_scores=True)
+    staged = tsa.scatter_residual(tsa.attn(*tsa.gather_qkv(q, k, v, idx)), idx, r)
+    assert torch.equal(out, staged)
+    assert torch.equal(tsa.score(q, k, 64), s_f)
+    assert torch.equal(tsa.select(s_f, keep, 64, 4), idx)
+
+
 def test_deterministic():
     x = workloads.small_random(1, 8, 2, 2000, 128, seed=3, dtype="bf16")
     q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")

@@ -29,6 +29,8 @@ int64_t forced_count(const tsa_desc& d) {
 
 bool empty_problem(const tsa_desc& d) { return d.B == 0 || d.L == 0; }
 
+bool fused_forward(const tsa_desc& d) { return d.dtype == TSA_BF16; }
+
 // Sizes, dtype and scale; keep/W/n_sink are checked separately (dense attention ignores them).
 tsa_status check_shape(const tsa_desc* d) {
   if (!d) return TSA_ERR_NULL;
@@ -111,13 +113,16 @@ Sizes sizes_of(const tsa_desc& d) {
   return z;
 }
 
-// Workspace carve-up of tsa_forward (regions in this order, each 256-byte aligned).
+// Workspace carve-up of tsa_forward (regions in this order, each 256-byte aligned).  The
+// bf16 forward is fused (attention reads the rows through idx and writes residual + O), so
+// it needs no compact tensors; the fp32 forward runs the stages one after the other.
 struct FwdLayout {
   size_t scores, idx, inv, part, stat, qh, kh, vh, oh, total;
 };
 
 FwdLayout fwd_layout(const tsa_desc& d) {
   const Sizes z = sizes_of(d);
+  const size_t comp = fused_forward(d) ? 0 : round_up(z.compact);
   FwdLayout f;
   size_t o = 0;
   f.scores = o; o += round_up(z.scores);
@@ -125,10 +130,10 @@ FwdLayout fwd_layout(const tsa_desc& d) {
   f.inv = o; o += round_up(z.inv);
   f.part = o; o += round_up(z.part);
   f.stat = o; o += round_up(z.stat);
-  f.qh = o; o += round_up(z.compact);
-  f.kh = o; o += round_up(z.compact);
-  f.vh = o; o += round_up(z.compact);
-  f.oh = o; o += round_up(z.compact);
+  f.qh = o; o += comp;
+  f.kh = o; o += comp;
+  f.vh = o; o += comp;
+  f.oh = o; o += comp;
   f.total = o;
   return f;
 }
@@ -300,6 +305,13 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   const bool in_place = out == residual;
   TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
   TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, s), s));
+  if (fused_forward(d)) {
+    // Rows no head keeps are the residual (copied out of place, untouched in place); the
+    // attention epilogue writes residual + O into the kept rows.
+    if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
+    if (d.keep == 0) return TSA_OK;
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, residual, out, s), s);
+  }
   if (d.keep > 0) {
     TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));
     TSA_TRY(after_launch(launch_attn_compact(d, qh, kh, vh, oh, s), s));

@@ -50,8 +50,11 @@ struct AttnParams {
   int kv_div;              // KV head of query head h is h / kv_div
   int BH, ntiles;
   float c;                 // logit scale * log2(e)
+  const int32_t* idx;      // fused forward: [B][H][n] positions of each head's rows
+  const void* res;         // fused forward: residual, same layout as o
 };
 
+constexpr int ATT_COMPACT = 0, ATT_DENSE = 1, ATT_FUSED = 2;
 constexpr int BN = 64;          // keys per tile
 constexpr int KB = BN / 32;     // 32-key blocks per tile
 constexpr float NEG_BIG = -3.0e38f;
@@ -332,8 +335,14 @@ __device__ __forceinline__ float half_swap(float x) {
   return __uint_as_float(__lane_id() < 32 ? pr[1] : pr[0]);
 }
 
-template <int D, int NW, bool DENSE>
+// MODE selects where rows live: ATT_COMPACT (contiguous [B][H][n][d] compact tensors),
+// ATT_DENSE ([B][L][H][d] and [B][L][Hkv][d], all L rows: the dense reference) or
+// ATT_FUSED (the compact rows are read through each head's index list straight from
+// [B][L][H][d] / [B][L][Hkv][d], and the epilogue writes residual + O into those rows of
+// the output: the fused forward, which never materialises Q^, K^, V^ or O^).
+template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) {
+  constexpr bool DENSE = MODE == ATT_DENSE, FUSED = MODE == ATT_FUSED, STRIDED = MODE != ATT_COMPACT;
   constexpr int NT = NW * TSA_WAVE;
   constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
@@ -349,8 +358,8 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   // Arguments in registers (lambdas capture by reference; a captured argument struct
   // would be placed in scratch memory).
   const int n = p.n;
-  const int64_t q_r = DENSE ? p.q_r : D, k_r = DENSE ? p.k_r : D, o_r = DENSE ? p.o_r : D;
-  const int kv_div = DENSE ? p.kv_div : 1;
+  const int64_t q_r = STRIDED ? p.q_r : D, k_r = STRIDED ? p.k_r : D, o_r = STRIDED ? p.o_r : D;
+  const int kv_div = STRIDED ? p.kv_div : 1;
   const float c = p.c;
 
   const int tid = threadIdx.x;
@@ -378,6 +387,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h;
   __bf16* obase = reinterpret_cast<__bf16*>(p.o) + b * p.o_b + h * p.o_h;
+  const int32_t* idx_bh = FUSED ? p.idx + (int64_t)bh * p.n : nullptr;
 
   const int q0 = tile * BM;
   const int wrow0 = q0 + wave * 32;
@@ -385,24 +395,39 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const int nkt = (min(n, q0 + BM) - 1) / BN + 1;
 
   // Staging: chunk i of this lane is row lrow[i], chunk lchunk[i] of the tile.
-  int lrow[LOADS], soff_k[LOADS], soff_v[LOADS];
+  int lrow[LOADS], lchunk[LOADS], soff_k[LOADS], soff_v[LOADS];
   const __bf16* kptr[LOADS];
   const __bf16* vptr[LOADS];
+  int pnext[LOADS];                                  // fused: positions of the next tile's rows
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int e = tid + NT * i;
-    const int ch = e % CPR;
+    lchunk[i] = e % CPR;
     lrow[i] = e / CPR;
-    soff_k[i] = lrow[i] * KP + ch * 16;
-    soff_v[i] = lrow[i] * VP + ch * 16;
-    kptr[i] = kbase + (int64_t)lrow[i] * k_r + ch * 8;
-    vptr[i] = vbase + (int64_t)lrow[i] * k_r + ch * 8;
+    soff_k[i] = lrow[i] * KP + lchunk[i] * 16;
+    soff_v[i] = lrow[i] * VP + lchunk[i] * 16;
+    kptr[i] = kbase + (int64_t)lrow[i] * k_r + lchunk[i] * 8;
+    vptr[i] = vbase + (int64_t)lrow[i] * k_r + lchunk[i] * 8;
+    if (FUSED) pnext[i] = idx_bh[min(lrow[i], n - 1)];
   }
   u32x4 kst[LOADS], vst[LOADS];
   int next_k0 = 0;
   // Loads the next tile into registers; rows past the end repeat the last row (they
-  // only meet queries that mask them).
+  // only meet queries that mask them).  Fused: the rows' positions were fetched one tile
+  // earlier, and this fetches the positions of the tile after.
   auto load_next = [&]() __attribute__((always_inline)) {
+    if (FUSED) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t off = (int64_t)pnext[i] * k_r + lchunk[i] * 8;
+        kst[i] = ld16(kbase + off);
+        vst[i] = ld16(vbase + off);
+      }
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) pnext[i] = idx_bh[min(next_k0 + BN + lrow[i], n - 1)];
+      next_k0 += BN;
+      return;
+    }
     if (next_k0 + BN <= n) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
@@ -429,7 +454,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   {
     const int row = wrow0 + lc;
     if (row < n)
-      qf.load(qbase + (int64_t)row * q_r + hf * (D / 2));
+      qf.load(qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + hf * (D / 2));
     else
       qf.zero();
   }
@@ -525,25 +550,47 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const float inv = 1.0f / (l + half_swap(l));
   const int i = wrow0 + lc;
   if (i < n) {
-    __bf16* orow = obase + (int64_t)i * o_r;
+    if (FUSED) {
+      // out = residual + O, with O first rounded to bf16 as the staged path stores it.
+      const int64_t roff = (int64_t)idx_bh[i] * o_r;
+      const __bf16* rrow = reinterpret_cast<const __bf16*>(p.res) + b * p.o_b + h * p.o_h + roff;
+      __bf16* orow = obase + roff;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * hf;
-        store4<__bf16>(orow + d0, o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                       o[db][4 * r4 + 3] * inv);
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + 8 * r4 + 4 * hf;
+          const u32x2 rv = *reinterpret_cast<const u32x2*>(rrow + d0);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ob = bf16_to_f32(f32_to_bf16(o[db][4 * r4 + e] * inv));
+            const uint32_t rb = (rv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            v[e] = bf16_to_f32(rb) + ob;
+          }
+          store4<__bf16>(orow + d0, v[0], v[1], v[2], v[3]);
+        }
+    } else {
+      __bf16* orow = obase + (int64_t)i * o_r;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + 8 * r4 + 4 * hf;
+          store4<__bf16>(orow + d0, o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                         o[db][4 * r4 + 3] * inv);
+        }
+    }
   }
 }
 
-template <int D, int NW, bool DENSE>
+template <int D, int NW, int MODE>
 hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW * 32;
   p.BH = B * H;
   p.ntiles = (p.n + BM - 1) / BM;
   const int64_t blocks = (int64_t)p.BH * p.ntiles;
-  attn_bf16_kernel<D, NW, DENSE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
+  attn_bf16_kernel<D, NW, MODE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -560,8 +607,8 @@ hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
 template <bool DENSE>
 hipError_t dispatch_attn(const tsa_desc& d, AttnParams p, hipStream_t s) {
   if (d.dtype == TSA_BF16) {
-    if (d.d == 128) return launch_attn_bf16<128, 8, DENSE>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_bf16<64, 8, DENSE>(p, d.B, d.H, s);
+    if (d.d == 128) return launch_attn_bf16<128, 8, DENSE ? ATT_DENSE : ATT_COMPACT>(p, d.B, d.H, s);
+    if (d.d == 64) return launch_attn_bf16<64, 8, DENSE ? ATT_DENSE : ATT_COMPACT>(p, d.B, d.H, s);
   } else {
     if (d.d == 128) return launch_attn_t<float, 128, 1, 4, DENSE>(p, d.B, d.H, s);
     if (d.d == 64) return launch_attn_t<float, 64, 1, 4, DENSE>(p, d.B, d.H, s);
@@ -588,6 +635,23 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
   p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
   p.c = attn_c(d);
   return dispatch_attn<false>(d, p, s);
+}
+
+hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                             const void* res, void* out, hipStream_t s) {
+  if (d.dtype != TSA_BF16) return hipErrorInvalidValue;
+  AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res;
+  p.n = d.keep;
+  p.H = d.H;
+  p.kv_div = d.H / d.Hkv;
+  p.q_r = (int64_t)d.H * d.d; p.q_h = d.d; p.q_b = (int64_t)d.L * d.H * d.d;
+  p.k_r = (int64_t)d.Hkv * d.d; p.k_h = d.d; p.k_b = (int64_t)d.L * d.Hkv * d.d;
+  p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
+  p.c = attn_c(d);
+  if (d.d == 128) return launch_attn_bf16<128, 8, ATT_FUSED>(p, d.B, d.H, s);
+  if (d.d == 64) return launch_attn_bf16<64, 8, ATT_FUSED>(p, d.B, d.H, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,

@@ -17,6 +17,11 @@ hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, co
                              void* qh, void* kh, void* vh, hipStream_t s);
 hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh, const void* vh, void* oh,
                                hipStream_t s);
+// Fused forward attention (bf16): compact rows read through idx, out rows = residual + O.
+hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                             const void* res, void* out, hipStream_t s);
+// Copies residual to out at the positions no head keeps (inverse map < 0), per head.
+hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s);
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
                              hipStream_t s);
 hipError_t launch_build_inverse(const tsa_desc& d, const int32_t* idx, int32_t* inv, hipStream_t s);

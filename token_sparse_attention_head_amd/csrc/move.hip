@@ -63,8 +63,9 @@ __device__ __forceinline__ u32x4 add_rows(u32x4 r, u32x4 o, tsa_dtype dt) {
 }
 
 // Out-of-place: one pass over [B][L][H] rows in memory order.  inv[b][h][p] is the
-// compact row of position p in S_h, or -1.
-template <int ROWB, tsa_dtype DT>
+// compact row of position p in S_h, or -1.  SKIP_KEPT leaves kept rows untouched (the fused
+// forward writes them from its attention epilogue).
+template <int ROWB, tsa_dtype DT, bool SKIP_KEPT = false>
 __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __restrict__ oh,
                                                                const int32_t* __restrict__ inv,
                                                                const char* __restrict__ res, char* __restrict__ out,
@@ -78,10 +79,11 @@ __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __res
   const int p = row / H;
   const int h = row % H;
   const int64_t off = ((b * L + p) * H + h) * ROWB + c * 16;
-  const u32x4 r = ld16_nt(res + off);
   const int t = inv[(b * H + h) * L + p];
+  if (SKIP_KEPT && t >= 0) return;
+  const u32x4 r = ld16_nt(res + off);
   u32x4 o = r;
-  if (t >= 0) o = add_rows(r, ld16(oh + (((b * H + h) * keep + t) * ROWB + c * 16)), DT);
+  if (!SKIP_KEPT && t >= 0) o = add_rows(r, ld16(oh + (((b * H + h) * keep + t) * ROWB + c * 16)), DT);
   st16_nt(out + off, o);
 }
 
@@ -158,6 +160,14 @@ hipError_t launch_scatter_residual(const tsa_desc& d, const void* oh, const int3
     TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_F32><<<grid, 256, 0, s>>>(
                                 (const char*)oh, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s) {
+  const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
+  const dim3 grid(blocks_for((int64_t)d.L * d.H * (rowb / 16)), d.B);
+  TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_BF16, true><<<grid, 256, 0, s>>>(
+                              nullptr, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
   return hipGetLastError();
 }
 
