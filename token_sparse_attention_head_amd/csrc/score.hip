@@ -92,9 +92,10 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(const T* __restrict__ 
   const int j_beg = ch * g.chunk;
   const int j_end = min(g.L, j_beg + g.chunk);
   const int first_row_pos = g.L - g.Wp;
+  HalfRow<T, D> kf, kn;                        // current and prefetched key tile
+  load_key<T, D>(k, g, b, kvh, j_beg + (lane & 31), lane, kf);
   for (int j0 = j_beg; j0 < j_end; j0 += 32) {
-    HalfRow<T, D> kf;
-    load_key<T, D>(k, g, b, kvh, j0 + (lane & 31), lane, kf);
+    if (j0 + 32 < j_end) load_key<T, D>(k, g, b, kvh, j0 + 32 + (lane & 31), lane, kn);
     const bool need_mask = j0 + 31 > first_row_pos;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(const T* __restrict__ 
       s[rb] = s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + add;
       m[rb] = mn;
     }
+    kf = kn;
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -129,21 +131,35 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(const T* __restrict__ 
   }
 }
 
-// Folds the per-chunk (max, sum) of every window row into (m_i, 1 / l_i), in chunk order.
-__global__ __launch_bounds__(64) void score_merge_kernel(const float2* __restrict__ part, float2* __restrict__ stat,
-                                                         int nchunk, int Wp) {
+// Folds the per-chunk (max, sum) of every window row into (m_i, 1 / l_i).  Four threads
+// per row each fold a strided quarter of the chunks, then the first folds the four
+// partials; the order is fixed, so the result is deterministic.
+constexpr int MERGE_PARTS = 4;
+__global__ __launch_bounds__(64 * MERGE_PARTS) void score_merge_kernel(const float2* __restrict__ part,
+                                                                       float2* __restrict__ stat, int nchunk,
+                                                                       int Wp) {
+  __shared__ float2 partial[MERGE_PARTS][64];
   const int bh = blockIdx.x;
-  const int row = threadIdx.x;
-  if (row >= Wp) return;
+  const int row = threadIdx.x % 64;
+  const int q = threadIdx.x / 64;
   const float2* p = part + (int64_t)bh * nchunk * Wp + row;
-  float M = NEG_BIG;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[(int64_t)c * Wp].x);
-  float S = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    const float2 v = p[(int64_t)c * Wp];
-    S += v.y * __builtin_amdgcn_exp2f(v.x - M);
+  float M = NEG_BIG, S = 0.f;
+  if (row < Wp) {
+    for (int c = q; c < nchunk; c += MERGE_PARTS) M = fmaxf(M, p[(int64_t)c * Wp].x);
+    for (int c = q; c < nchunk; c += MERGE_PARTS) {
+      const float2 v = p[(int64_t)c * Wp];
+      S += v.y * __builtin_amdgcn_exp2f(v.x - M);
+    }
   }
-  stat[(int64_t)bh * Wp + row] = make_float2(M, 1.0f / S);
+  partial[q][row] = make_float2(M, S);
+  __syncthreads();
+  if (q == 0 && row < Wp) {
+    float Mt = NEG_BIG;
+    for (int i = 0; i < MERGE_PARTS; ++i) Mt = fmaxf(Mt, partial[i][row].x);
+    float St = 0.f;
+    for (int i = 0; i < MERGE_PARTS; ++i) St += partial[i][row].y * __builtin_amdgcn_exp2f(partial[i][row].x - Mt);
+    stat[(int64_t)bh * Wp + row] = make_float2(Mt, 1.0f / St);
+  }
 }
 
 template <typename T, int D, int RB>
@@ -181,10 +197,11 @@ __global__ __launch_bounds__(256) void score_pass2_kernel(const T* __restrict__ 
   const int j_end = min(g.L, j_beg + g.chunk);
   const int first_row_pos = g.L - g.Wp;
   float* out = scores + ((int64_t)b * g.H + h) * g.L;
+  HalfRow<T, D> kf, kn;                        // current and prefetched key tile
+  load_key<T, D>(k, g, b, kvh, j_beg + (lane & 31), lane, kf);
   for (int j0 = j_beg; j0 < j_end; j0 += 32) {
-    HalfRow<T, D> kf;
     const int j = j0 + (lane & 31);
-    load_key<T, D>(k, g, b, kvh, j, lane, kf);
+    if (j0 + 32 < j_end) load_key<T, D>(k, g, b, kvh, j + 32, lane, kn);
     const bool need_mask = j0 + 31 > first_row_pos;
     float col = 0.f;
 #pragma unroll
@@ -201,6 +218,7 @@ __global__ __launch_bounds__(256) void score_pass2_kernel(const T* __restrict__ 
     }
     col += xor32(col);
     if (hf == 0 && j < g.L) out[j] = col;
+    kf = kn;
   }
 }
 
@@ -222,7 +240,7 @@ hipError_t launch_score_t(const tsa_desc& d, const void* q, const void* k, float
   } else {
     score_pass1_kernel<T, D, 1><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, part, g, c);
   }
-  score_merge_kernel<<<d.B * d.H, 64, 0, s>>>(part, stat, g.nchunk, g.Wp);
+  score_merge_kernel<<<d.B * d.H, 64 * MERGE_PARTS, 0, s>>>(part, stat, g.nchunk, g.Wp);
   if (g.Wp > 32) {
     score_pass2_kernel<T, D, 2><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, stat, scores, g, c);
   } else {
