@@ -260,6 +260,25 @@ def test_fused_forward_equals_staged(B, H, Hkv, L, d, keep, in_place):
     assert torch.equal(tsa.select(s_f, keep, 64, 4), idx)
 
 
+@pytest.mark.parametrize("L,keep,W,ns", [
+    (40, 40, 64, 4),        # window covers the sequence, one partial key tile
+    (65, 36, 32, 4),        # keep = |F|: no score-chosen token; a ragged second tile
+    (200, 200, 64, 4),      # keep = L: sparse must equal dense
+    (129, 70, 1, 1),        # one-row window
+    (8, 3, 1, 1),           # the tiny case
+])
+def test_fused_forward_edge_cases(L, keep, W, ns):
+    x = workloads.small_random(1, 4, 2, L, 128, seed=L, dtype="bf16")
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    out, s_f, idx = tsa.forward(q, k, v, r, keep, W, ns, return_scores=True)
+    staged = tsa.scatter_residual(tsa.attn(*tsa.gather_qkv(q, k, v, idx)), idx, r)
+    assert torch.equal(out, staged)
+    _end_to_end(x, "bf16", keep, W, ns)
+    if keep == L:
+        dense = tsa.dense_attn(q, k, v).float() + r.float()
+        assert float((out.float() - dense).abs().max()) <= 2e-2 + 0.0625
+
+
 def test_deterministic():
     x = workloads.small_random(1, 8, 2, 2000, 128, seed=3, dtype="bf16")
     q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
