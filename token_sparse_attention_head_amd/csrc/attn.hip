@@ -15,21 +15,23 @@
 //   wave keeps its QB blocks of 32 query rows in registers as MFMA operands.  The bf16
 //   kernel runs 8 waves (2 per SIMD) within 256 registers each, so one wave's softmax
 //   arithmetic issues while the other wave's matrix instructions run.
-// * Key/value tiles of 64 rows stream through LDS, double buffered, with the next
-//   tile's global loads in flight while the current tile is on the matrix cores.
+// * Key/value tiles of 64 rows stream through LDS, double buffered; the global loads of
+//   the next two tiles are in flight in registers while the current tile is on the
+//   matrix cores.
 // * Scores are formed transposed, S^T = K Q^T (32x32x16 bf16 MFMA), so a lane owns one
-//   query and 16 keys per 32-key block: the softmax row max needs one cross-half
-//   exchange per tile and the row sum stays lane-local.
+//   query and 16 keys per 32-key block and the row sums stay lane-local.
 // * O^T = V^T P^T: the probabilities a lane already holds are the B operand as they
-//   are; V is written to LDS transposed, with keys permuted inside each 16-key group
-//   to match, so every operand read is one 16-byte LDS read.  16-byte chunks are
-//   XOR-swizzled so the 32 rows a wave reads at once fall in different banks.
-// * Online softmax in exp2 units with lazy rescaling: the running max moves (and O, l
-//   are rescaled) only when a row's max grows by more than 2^8, which keeps every
-//   probability below 256 and skips almost all rescales on long rows.
+//   are, and V^T is read from V's natural [key][d] rows with the transposing LDS read
+//   ds_read_b64_tr_b16.  LDS rows are padded (K: 2d + 16 bytes, V: 2d + 64 bytes) so
+//   neither operand read has bank conflicts.
+// * Online softmax in exp2 units against a lazily moved reference: a tile's
+//   probabilities are taken against the current reference without a row max, and the
+//   tile's probability sum tells whether that was safe (below 2^32 nothing is near
+//   overflow).  Only when it is not (the first tile, or a row max that jumped) does the
+//   exact max move the reference and rescale O and l.
 // * Query tiles are issued longest first; all tiles of a head go to one XCD (workgroup
-//   IDs are dealt to the 8 XCDs round-robin) so the K/V tiles they share hit in that
-//   XCD's L2.
+//   IDs are dealt to the 8 XCDs round-robin) and an XCD runs one head's tiles before the
+//   next head's, so its concurrent workgroups stream the same K/V tiles through its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -212,8 +214,8 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
     if (p.BH % 8 == 0) {
       const int hpx = p.BH / 8;
       const int x = bid % 8, sl = bid / 8;
-      bh = x * hpx + sl % hpx;
-      tile = p.ntiles - 1 - sl / hpx;
+      bh = x * hpx + sl / p.ntiles;
+      tile = p.ntiles - 1 - sl % p.ntiles;
     } else {
       bh = bid % p.BH;
       tile = p.ntiles - 1 - bid / p.BH;
@@ -373,8 +375,8 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
     if (p.BH % 8 == 0) {
       const int hpx = p.BH / 8;
       const int x = bid % 8, sl = bid / 8;
-      bh = x * hpx + sl % hpx;
-      tile = p.ntiles - 1 - sl / hpx;
+      bh = x * hpx + sl / p.ntiles;
+      tile = p.ntiles - 1 - sl % p.ntiles;
     } else {
       bh = bid % p.BH;
       tile = p.ntiles - 1 - bid / p.BH;
@@ -410,18 +412,19 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
     vptr[i] = vbase + (int64_t)lrow[i] * k_r + lchunk[i] * 8;
     if (FUSED) pnext[i] = idx_bh[min(lrow[i], n - 1)];
   }
-  u32x4 kst[LOADS], vst[LOADS];
+  constexpr int PF = 2;                              // tiles in flight in registers
+  u32x4 kst[PF][LOADS], vst[PF][LOADS];
   int next_k0 = 0;
   // Loads the next tile into registers; rows past the end repeat the last row (they
   // only meet queries that mask them).  Fused: the rows' positions were fetched one tile
   // earlier, and this fetches the positions of the tile after.
-  auto load_next = [&]() __attribute__((always_inline)) {
+  auto load_next = [&](int set) __attribute__((always_inline)) {
     if (FUSED) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int64_t off = (int64_t)pnext[i] * k_r + lchunk[i] * 8;
-        kst[i] = ld16(kbase + off);
-        vst[i] = ld16(vbase + off);
+        kst[set][i] = ld16(kbase + off);
+        vst[set][i] = ld16(vbase + off);
       }
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) pnext[i] = idx_bh[min(next_k0 + BN + lrow[i], n - 1)];
@@ -431,15 +434,15 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
     if (next_k0 + BN <= n) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        kst[i] = ld16(kptr[i]);
-        vst[i] = ld16(vptr[i]);
+        kst[set][i] = ld16(kptr[i]);
+        vst[set][i] = ld16(vptr[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int64_t back = (int64_t)(max(next_k0 + lrow[i] - (n - 1), 0)) * k_r;
-        kst[i] = ld16(kptr[i] - back);
-        vst[i] = ld16(vptr[i] - back);
+        kst[set][i] = ld16(kptr[i] - back);
+        vst[set][i] = ld16(vptr[i] - back);
       }
     }
 #pragma unroll
@@ -467,14 +470,14 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
-  auto step = [&](int t, Buf& cur) __attribute__((always_inline)) {
+  auto step = [&](int t, Buf& cur, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4*>(cur.k + soff_k[i]) = kst[i];
-      *reinterpret_cast<u32x4*>(cur.v + soff_v[i]) = vst[i];
+      *reinterpret_cast<u32x4*>(cur.k + soff_k[i]) = kst[set][i];
+      *reinterpret_cast<u32x4*>(cur.v + soff_v[i]) = vst[set][i];
     }
     __syncthreads();
-    if (t + 1 < nkt) load_next();
+    if (t + PF < nkt) load_next(set);
     const int k0 = t * BN;
     if (wrow0 > wave_last || k0 > wave_last) return;   // no key of this tile is visible
 
@@ -490,45 +493,49 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
     }
 
     // Online softmax of the tile (mask only where the tile reaches the diagonal).
+    // Probabilities against the running reference m; the tile's probability sum
+    // guards it (below 2^32 nothing is near overflow), else the exact max rescales.
     const bool diag = k0 + BN - 1 > wrow0;
-    const int lim = wrow0 + lc - k0 - 4 * hf;
-    float tmax = -__builtin_huge_valf();
     if (diag) {
+      const int lim = wrow0 + lc - k0 - 4 * hf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, 0) > lim - 32 * kb) s[kb][r] = -__builtin_huge_valf();
+    }
+    bf16x8 pf[KB][2];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    auto probs = [&](float mref) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (acc_row(r, 0) > lim - 32 * kb) s[kb][r] = -__builtin_huge_valf();
-          tmax = fmaxf(tmax, s[kb][r]);
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mref));
+          ls[r & 3] += pr;
+          pf[kb][r >> 3][r & 7] = static_cast<__bf16>(pr);
         }
-    } else {
+    };
+    probs(m);
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if (__ballot(!(lsum < 4294967296.0f)) != 0) {
+      float tmax = -__builtin_huge_valf();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-    }
-    tmax = fmaxf(tmax, half_swap(tmax));
-    const float mt = tmax * c;
-    if (__ballot(mt > m + RESCALE_SLACK) != 0) {
-      const float mn = fmaxf(m, mt);
+      tmax = fmaxf(tmax, half_swap(tmax));
+      const float mn = fmaxf(m, tmax * c);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m = mn;
+      ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
+      probs(mn);
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    bf16x8 pf[KB][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m));
-        lsum += pr;
-        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(pr);
-      }
     l += lsum;
-
     // O^T += V^T P^T.
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -541,10 +548,11 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
         }
   };
 
-  load_next();
+  load_next(0);
+  if (PF == 2 && nkt > 1) load_next(PF - 1);
   for (int t = 0; t < nkt; t += 2) {
-    step(t, lds[0]);
-    if (t + 1 < nkt) step(t + 1, lds[1]);
+    step(t, lds[0], 0);
+    if (t + 1 < nkt) step(t + 1, lds[1], PF - 1);
   }
 
   const float inv = 1.0f / (l + half_swap(l));
