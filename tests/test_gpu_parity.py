@@ -97,6 +97,30 @@ def test_attn_compact(dt, d, n):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 64), ("fp32", 128)])
+def test_attn_logit_jumps(dt, d):
+    # Keys aligned with every query at a few late positions make a row's logits jump by
+    # more than 32 in log2 units mid-row (the running softmax reference must move and O
+    # be rescaled there), and an early huge logit makes every later probability tiny.
+    B, H, n = 1, 2, 700
+    rng = np.random.default_rng(11 + d)
+    u = np.ones(d) / np.sqrt(d)
+    qh = rng.standard_normal((B, H, n, d)) * 0.3 + 8.0 * u
+    kh = rng.standard_normal((B, H, n, d)) * 0.3
+    vh = rng.standard_normal((B, H, n, d))
+    kh[:, 0, 5] = 60.0 * u                     # head 0: early dominant key
+    for pos, b in ((150, 40.0), (400, 80.0), (650, 120.0)):
+        kh[:, 1, pos] = b * u                  # head 1: jumps of ~40 log2 units each
+    qh, kh, vh = (t.astype(np.float32) for t in (qh, kh, vh))
+    if dt == "bf16":
+        qh, kh, vh = (workloads.round_bf16(t) for t in (qh, kh, vh))
+    oh = tsa.attn(dev(qh, dt), dev(kh, dt), dev(vh, dt))
+    want = oracle.attend(qh, kh, vh)
+    err = np.max(np.abs(host(oh) - want))
+    print(f"attn jumps {dt} d={d}: max abs err {err:.3e}")
+    assert err <= TOL[dt]
+
+
 @pytest.mark.parametrize("dt,d,H,Hkv,L", [("bf16", 128, 8, 2, 777), ("bf16", 128, 4, 4, 200), ("fp32", 64, 4, 1, 390)])
 def test_dense_attn(dt, d, H, Hkv, L):
     x = workloads.small_random(1, H, Hkv, L, d, seed=8, dtype=dt)

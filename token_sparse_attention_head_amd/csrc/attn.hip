@@ -420,14 +420,21 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   // earlier, and this fetches the positions of the tile after.
   auto load_next = [&](int set) __attribute__((always_inline)) {
     if (FUSED) {
+      // The next tile's positions are requested before this tile's rows: loads complete
+      // in order, so waiting for the positions later does not wait for the rows.
+      int pcur[LOADS];
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int64_t off = (int64_t)pnext[i] * k_r + lchunk[i] * 8;
+        pcur[i] = pnext[i];
+        pnext[i] = idx_bh[min(next_k0 + BN + lrow[i], n - 1)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t off = (int64_t)pcur[i] * k_r + lchunk[i] * 8;
         kst[set][i] = ld16(kbase + off);
         vst[set][i] = ld16(vbase + off);
       }
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) pnext[i] = idx_bh[min(next_k0 + BN + lrow[i], n - 1)];
       next_k0 += BN;
       return;
     }
@@ -470,6 +477,18 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](const Buf& buf, const bf16x8 (&pf)[KB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const char* a = buf.v + (kb * 32 + 16 * jj) * VP + voff + db * 64;
+          o[db] = mfma(o[db], tr_read2(a, a + 8 * VP), pf[kb][jj]);
+        }
+  };
   auto step = [&](int t, Buf& cur, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -477,19 +496,24 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
       *reinterpret_cast<u32x4*>(cur.v + soff_v[i]) = vst[set][i];
     }
     __syncthreads();
-    if (t + PF < nkt) load_next(set);
+    // Unconditional (past the end it re-reads the clamped last rows): every step then
+    // issues the same loads, so the wait before a store only waits for that tile.
+    load_next(set);
     const int k0 = t * BN;
     if (wrow0 > wave_last || k0 > wave_last) return;   // no key of this tile is visible
 
     f32x16 s[KB];
+    // Each 32-key block's eight K operands are read before its MFMAs so the reads
+    // overlap one another instead of each MFMA waiting for its own.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 kf[D / 16];
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) kf[s2] = *reinterpret_cast<const bf16x8*>(cur.k + kb * 32 * KP + koff + s2 * 16);
+      __builtin_amdgcn_sched_barrier(0);
       s[kb] = f32x16{};
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cur.k + kb * 32 * KP + koff + s2 * 16);
-        s[kb] = mfma(s[kb], kf, qf.f[s2]);
-      }
+      for (int s2 = 0; s2 < D / 16; ++s2) s[kb] = mfma(s[kb], kf[s2], qf.f[s2]);
     }
 
     // Online softmax of the tile (mask only where the tile reaches the diagonal).
@@ -536,23 +560,16 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
       lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     l += lsum;
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const char* a = cur.v + (kb * 32 + 16 * jj) * VP + voff + db * 64;
-          o[db] = mfma(o[db], tr_read2(a, a + 8 * VP), pf[kb][jj]);
-        }
+    pv(cur, pf);
   };
 
   load_next(0);
-  if (PF == 2 && nkt > 1) load_next(PF - 1);
+  if (PF == 2) load_next(PF - 1);
+  // Steps run in pairs; a step past the last tile only stages and meets the barrier
+  // (no wave sees its keys), which keeps the loop body free of conditions.
   for (int t = 0; t < nkt; t += 2) {
     step(t, lds[0], 0);
-    if (t + 1 < nkt) step(t + 1, lds[1], PF - 1);
+    step(t + 1, lds[1], PF - 1);
   }
 
   const float inv = 1.0f / (l + half_swap(l));
@@ -563,12 +580,18 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
       const int64_t roff = (int64_t)idx_bh[i] * o_r;
       const __bf16* rrow = reinterpret_cast<const __bf16*>(p.res) + b * p.o_b + h * p.o_h + roff;
       __bf16* orow = obase + roff;
+      u32x2 rvs[D / 32][4];                       // all residual reads in flight at once
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) rvs[db][r4] = *reinterpret_cast<const u32x2*>(rrow + db * 32 + 8 * r4 + 4 * hf);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d0 = db * 32 + 8 * r4 + 4 * hf;
-          const u32x2 rv = *reinterpret_cast<const u32x2*>(rrow + d0);
+          const u32x2 rv = rvs[db][r4];
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
