@@ -27,6 +27,13 @@ Figure 3 and the Abstract):
                     every other position, and the residual added everywhere (Figure 3:
                     scatter back to the full layout, then add the residual).
 
+Subsets per KV head (``per_kv_head`` / ``kv_heads``): an extension of the library, not
+from the pages, which define per-head subsets only.  The G query heads of KV head g share
+one subset S_g, chosen by the same rule as a per-head subset but on ``group_scores``: the
+sum of the G heads' score rows, taken in ascending head order in the scores' own dtype.
+Every other stage is unchanged except that head h uses S_{h // G} and the compact K/V
+rows are held once per subset.
+
 Every function works in float64; bf16 and fp32 inputs widen to float64 exactly.
 The readings taken where the pages are silent (window, causality, ties, order, the
 residual everywhere, the GQA head map, scale 1/sqrt(head_dim)) are stated at each
@@ -38,7 +45,7 @@ import numpy as np
 
 __all__ = [
     "window", "forced_positions", "score", "score_head", "select", "select_row",
-    "gather", "attend", "attend_rows", "scatter_residual", "forward", "threshold",
+    "gather", "attend", "attend_rows", "scatter_residual", "forward", "threshold", "group_scores",
 ]
 
 
@@ -116,14 +123,35 @@ def select_row(s_row, keep: int, W: int, n_sink: int) -> np.ndarray:
     return np.sort(np.concatenate([F, chosen]))
 
 
-def select(s, keep: int, W: int, n_sink: int) -> np.ndarray:
-    """idx [B,H,keep] (int64, strictly ascending per head) from scores [B,H,L]."""
+def group_scores(s, kv_heads: int) -> np.ndarray:
+    """[B,H,L] -> [B,kv_heads,L]: row g is the sum of the score rows of query heads
+    g*G .. g*G+G-1, added one head at a time in ascending order, in the dtype of ``s``
+    (a float32 input is summed in float32, as the kernel does, so the two rank the
+    positions identically)."""
+    s = np.asarray(s)
+    B, H, L = s.shape
+    G = H // kv_heads
+    out = np.empty((B, kv_heads, L), dtype=s.dtype)
+    for g in range(kv_heads):
+        acc = s[:, g * G, :].copy()
+        for j in range(1, G):
+            acc = acc + s[:, g * G + j, :]
+        out[:, g, :] = acc
+    return out
+
+
+def select(s, keep: int, W: int, n_sink: int, kv_heads: int | None = None) -> np.ndarray:
+    """idx [B,R,keep] (int64, strictly ascending per subset) from scores [B,H,L]: one
+    subset per query head (R = H), or with ``kv_heads`` one per KV head on
+    ``group_scores`` (R = kv_heads)."""
+    if kv_heads is not None:
+        s = group_scores(s, kv_heads)
     s = np.asarray(s, dtype=np.float64)
-    B, H, _ = s.shape
-    idx = np.empty((B, H, keep), dtype=np.int64)
+    B, R, _ = s.shape
+    idx = np.empty((B, R, keep), dtype=np.int64)
     for b in range(B):
-        for h in range(H):
-            idx[b, h] = select_row(s[b, h], keep, W, n_sink)
+        for r in range(R):
+            idx[b, r] = select_row(s[b, r], keep, W, n_sink)
     return idx
 
 
@@ -142,21 +170,25 @@ def threshold(s_row, keep: int, W: int, n_sink: int) -> float:
 
 
 def gather(q, k, v, idx):
-    """Q^[b,h,t] = Q[b,S_t,h]; K^[b,h,t] = K[b,S_t,g]; V^[b,h,t] = V[b,S_t,g], g = h // G
-    (skill page, Step 2, gather by index; Figure 3, stage 1).  -> three [B,H,keep,d]."""
+    """Q^[b,h,t] = Q[b,S_t,h]; K^[b,r,t] = K[b,S_t,g]; V^[b,r,t] = V[b,S_t,g], where
+    query head h uses subset r = h // (H/R) and g = h // G is its KV head (skill page,
+    Step 2, gather by index; Figure 3, stage 1).  idx [B,R,keep] -> Q^ [B,H,keep,d],
+    K^, V^ [B,R,keep,d] (R = H: per head, one copy of the K/V rows per query head)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, L, H, d = q.shape
     G = H // k.shape[2]
-    keep = idx.shape[2]
+    R, keep = idx.shape[1], idx.shape[2]
+    SG = H // R
     qh = np.empty((B, H, keep, d))
-    kh = np.empty((B, H, keep, d))
-    vh = np.empty((B, H, keep, d))
+    kh = np.empty((B, R, keep, d))
+    vh = np.empty((B, R, keep, d))
     for b in range(B):
         for h in range(H):
-            sel = idx[b, h]
-            qh[b, h] = q[b, sel, h, :]
-            kh[b, h] = k[b, sel, h // G, :]
-            vh[b, h] = v[b, sel, h // G, :]
+            qh[b, h] = q[b, idx[b, h // SG], h, :]
+        for r in range(R):
+            g = (r * SG) // G
+            kh[b, r] = k[b, idx[b, r], g, :]
+            vh[b, r] = v[b, idx[b, r], g, :]
     return qh, kh, vh
 
 
@@ -182,12 +214,13 @@ def attend(qh, kh, vh, scale: float | None = None) -> np.ndarray:
     original positions because S_h is ascending."""
     qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
     B, H, n, d = qh.shape
+    SG = H // kh.shape[1]                     # query heads per K^/V^ row block
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     oh = np.empty_like(qh)
     rows = np.arange(n)
     for b in range(B):
         for h in range(H):
-            oh[b, h] = _attend_head(qh[b, h], kh[b, h], vh[b, h], scale, rows)
+            oh[b, h] = _attend_head(qh[b, h], kh[b, h // SG], vh[b, h // SG], scale, rows)
     return oh
 
 
@@ -203,18 +236,20 @@ def scatter_residual(oh, idx, r) -> np.ndarray:
     oh, r = _f64(oh), _f64(r)
     out = r.copy()
     B, H, n, _ = oh.shape
+    SG = H // idx.shape[1]                    # query heads per subset
     for b in range(B):
         for h in range(H):
-            out[b, idx[b, h], h, :] += oh[b, h]
+            out[b, idx[b, h // SG], h, :] += oh[b, h]
     return out
 
 
-def forward(q, k, v, r, keep: int, W: int, n_sink: int, scale: float | None = None) -> dict:
+def forward(q, k, v, r, keep: int, W: int, n_sink: int, scale: float | None = None,
+            per_kv_head: bool = False) -> dict:
     """All five stages; returns scores, idx, the compact tensors, O^ and Out."""
     d = np.asarray(q).shape[-1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     s = score(q, k, W, scale)
-    idx = select(s, keep, W, n_sink)
+    idx = select(s, keep, W, n_sink, np.asarray(k).shape[2] if per_kv_head else None)
     qh, kh, vh = gather(q, k, v, idx)
     oh = attend(qh, kh, vh, scale)
     out = scatter_residual(oh, idx, r)

@@ -248,3 +248,90 @@ def test_inputs_reproducible_and_bf16_exact():
     raw = np.random.default_rng(0).standard_normal(1000, dtype=np.float32)
     want = torch.from_numpy(raw).to(torch.bfloat16).float().numpy()
     assert np.array_equal(workloads.round_bf16(raw), want)   # our RNE equals torch's
+
+
+# ---- subsets per KV head (an extension of the library: the pages define per-head subsets) ----
+
+def test_group_select_hand_case():
+    # Query heads 0 and 1 share KV head 0; L = 8, one sink and a window of one: F = {0, 7}.
+    # Worked by hand: the summed row is [0, 5, 5, 4, 4, 0, 0, 0].  keep 4 takes the two
+    # fives (positions 1, 2); keep 5 also takes one of the tied fours, the lower (3).  Per
+    # head the subsets differ: head 0 takes 1 (5) and 4 (2), head 1 takes 2 and 3 (4, 4).
+    s = np.zeros((1, 2, 8))
+    s[0, 0] = [0, 5, 1, 0, 2, 0, 0, 0]
+    s[0, 1] = [0, 0, 4, 4, 2, 0, 0, 0]
+    assert oracle.select(s, 4, 1, 1, kv_heads=1).tolist() == [[[0, 1, 2, 7]]]
+    assert oracle.select(s, 5, 1, 1, kv_heads=1).tolist() == [[[0, 1, 2, 3, 7]]]
+    assert oracle.select(s, 4, 1, 1).tolist() == [[[0, 1, 4, 7], [0, 2, 3, 7]]]
+
+
+def test_group_select_identical_heads_and_g1():
+    rng = np.random.default_rng(11)
+    base = np.round(rng.random((2, 3, 40)) * 8) / 4            # quarter steps: sums stay exact, many ties
+    s = np.repeat(base, 4, axis=1)                              # 3 KV heads x 4 identical query heads
+    shared = oracle.select(s, 20, 5, 4, kv_heads=3)
+    per_head = oracle.select(base, 20, 5, 4)
+    assert np.array_equal(shared, per_head)
+    # one query head per KV head: the shared rule is the per-head rule
+    assert np.array_equal(oracle.select(base, 20, 5, 4, kv_heads=3), per_head)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_group_select_exchange_property(seed):
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(8, 40))
+    W = int(rng.integers(1, 6))
+    n_sink = int(rng.integers(0, 5))
+    nF = len(oracle.forced_positions(L, W, n_sink))
+    keep = int(rng.integers(nF, L + 1))
+    s = np.round(rng.random((1, 4, L)) * 4) / 4                 # 2 KV heads x 2 query heads, ties
+    idx = oracle.select(s, keep, W, n_sink, kv_heads=2)
+    for g in range(2):
+        summed = s[0, 2 * g] + s[0, 2 * g + 1]                  # exact in quarter steps
+        _check_subset(summed, idx[0, g], keep, W, n_sink)
+
+
+def test_group_gather_scatter_brute_force():
+    x = workloads.small_random(2, 4, 2, 9, 3, seed=7)            # G = 2: subsets r = h // 2
+    idx = np.array([[[0, 2, 5, 8], [1, 2, 3, 8]], [[0, 4, 7, 8], [3, 5, 6, 8]]])
+    qh, kh, vh = oracle.gather(x["q"], x["k"], x["v"], idx)
+    assert qh.shape == (2, 4, 4, 3) and kh.shape == (2, 2, 4, 3)
+    oh = np.random.default_rng(1).standard_normal(qh.shape)
+    out = oracle.scatter_residual(oh, idx, x["r"])
+    for b in range(2):
+        for h in range(4):
+            sub = idx[b, h // 2].tolist()
+            for t in range(4):
+                for c in range(3):
+                    assert qh[b, h, t, c] == x["q"][b, sub[t], h, c]
+                    assert kh[b, h // 2, t, c] == x["k"][b, sub[t], h // 2, c]
+                    assert vh[b, h // 2, t, c] == x["v"][b, sub[t], h // 2, c]
+            for p in range(9):
+                for c in range(3):
+                    want = float(x["r"][b, p, h, c])
+                    if p in sub:
+                        want += oh[b, h, sub.index(p), c]
+                    assert out[b, p, h, c] == want
+
+
+def test_group_attend_equals_repeated_rows():
+    rng = np.random.default_rng(4)
+    qh = rng.standard_normal((1, 4, 30, 8))
+    kh = rng.standard_normal((1, 2, 30, 8))
+    vh = rng.standard_normal((1, 2, 30, 8))
+    shared = oracle.attend(qh, kh, vh)
+    repeated = oracle.attend(qh, np.repeat(kh, 2, axis=1), np.repeat(vh, 2, axis=1))   # per-head form, pinned by SDPA
+    assert np.array_equal(shared, repeated)
+
+
+def test_group_forward_equals_per_head_when_queries_coincide():
+    # If the query heads of a KV head carry the same queries, their scores coincide, so the
+    # shared subset is each head's own subset and the whole layer agrees with per-head mode.
+    x = workloads.small_random(1, 4, 2, 48, 8, seed=9)
+    q = x["q"].copy()
+    q[:, :, 1] = q[:, :, 0]
+    q[:, :, 3] = q[:, :, 2]
+    a = oracle.forward(q, x["k"], x["v"], x["r"], 20, 6, 2, per_kv_head=True)
+    b = oracle.forward(q, x["k"], x["v"], x["r"], 20, 6, 2)
+    assert np.array_equal(a["idx"][:, [0, 0, 1, 1]], b["idx"])
+    assert np.array_equal(a["out"], b["out"])
