@@ -90,26 +90,30 @@ def measured_traffic(workload):
     return float(fields["hbm_bytes_per_launch"])
 
 
-def algorithmic(w):
-    """Work the method must do per stage (flops or bytes), as defined for the roofline."""
+def algorithmic(w, per_kv_head=False):
+    """Work the method must do per stage (flops or bytes), as defined for the roofline.
+    With subsets per KV head the K/V rows are gathered once per subset (R = Hkv)."""
     e = 2 if w.dtype == "bf16" else 4
     B, H, Hkv, L, d, K, W = w.B, w.H, w.Hkv, w.L, w.d, w.keep, min(w.W, w.L)
+    R = Hkv if per_kv_head else H
     score_flops = 2.0 * B * H * d * sum(L - W + r + 1 for r in range(W)) * 2   # two passes over the window logits
     return {
         "score_flops": score_flops,
         "score_bytes": B * Hkv * L * d * e + B * H * W * d * e + 4 * B * H * L,
-        "select_bytes": 4 * B * H * (L + K),
-        "gather_bytes": 2 * 3 * B * H * K * d * e + 4 * B * H * K,
+        # scores read; per KV head also the summed rows written and read back; idx written
+        "select_bytes": 4 * B * H * L + (8 * B * R * L if R < H else 0) + 4 * B * R * K,
+        "gather_bytes": 2 * (B * H + 2 * B * R) * K * d * e + 4 * B * H * K,
         "attn_flops": 2.0 * B * H * d * K * (K + 1),
         "scatter_bytes": 2 * B * L * H * d * e + B * H * K * d * e + 4 * B * H * L,
         "dense_flops": 2.0 * B * H * d * L * (L + 1),
     }
 
 
-def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense):
+def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per_kv_head=False):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
-    desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink)
+    desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink, per_kv_head=per_kv_head)
+    R = w.Hkv if per_kv_head else w.H
     ws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(r)
     B, L, H, D = q.shape
@@ -126,13 +130,14 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense):
 
     # Stage by stage through the standalone entry points, same sizes and buffers.
     scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
-    idx = torch.empty(B, H, w.keep, dtype=torch.int32, device="cuda")
+    idx = torch.empty(B, R, w.keep, dtype=torch.int32, device="cuda")
     sws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCORE)), dtype=torch.uint8, device="cuda")
-    comp = [torch.empty(B, H, w.keep, D, dtype=dt, device="cuda") for _ in range(4)]
+    lws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SELECT)), dtype=torch.uint8, device="cuda")
+    comp = [torch.empty(B, n, w.keep, D, dtype=dt, device="cuda") for n in (H, R, R, H)]
     cws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCATTER)), dtype=torch.uint8, device="cuda")
     stages = {
         "score": lambda: tsa.tsa_score(desc, q, k, scores, sws),
-        "select": lambda: tsa.tsa_select(desc, scores, idx),
+        "select": lambda: tsa.tsa_select(desc, scores, idx, lws, lws.numel()),
         "gather": lambda: tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2]),
         "attn": lambda: tsa.tsa_attn(desc, comp[0], comp[1], comp[2], comp[3]),
         "scatter": lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r, out, cws),
@@ -146,9 +151,10 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense):
     stage_ms["scatter_inplace"] = timer.run(lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r2, r2), reps)
     del r2
 
-    res = {"workload": w.name, "keep": w.keep, "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events,
+    res = {"workload": w.name, "subsets": "per_kv_head" if per_kv_head else "per_head", "keep": w.keep,
+           "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events,
            "wall_ms_per_step": wall_ms, "tokens_per_s": B * L / (ms_events / 1e3), "stage_ms": stage_ms}
-    a = algorithmic(w)
+    a = algorithmic(w, per_kv_head)
     res["stage_rate"] = {
         "score_tflops": a["score_flops"] / (stage_ms["score"] * 1e-3) / 1e12,
         "select_gbs": a["select_bytes"] / (stage_ms["select"] * 1e-3) / 1e9,
@@ -292,6 +298,17 @@ def main():
                 res["speedup_vs_dense"] = head["dense_ms"] / res["ms_per_step"]
                 res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
             log(f"{wi.name}: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
+            sweep.append(res)
+        # The same keep ratios with one token subset per KV head (the library's extension).
+        for name in ("bf16_L128k_r0.5", "bf16_L128k_r0.25", "bf16_L128k_r0.1"):
+            wi = workloads.WORKLOADS[name]
+            res = gpu_case(tsa, torch, timer, wi, x, args, args.stage_reps, max(3, args.steps // 2), 1, False,
+                           per_kv_head=True)
+            if "dense_ms" in head:
+                res["dense_ms"] = head["dense_ms"]
+                res["speedup_vs_dense"] = head["dense_ms"] / res["ms_per_step"]
+                res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
+            log(f"{wi.name} per KV head: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
             sweep.append(res)
 
     a = algorithmic(w)

@@ -12,16 +12,23 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Sizes (tsa_desc):  B batch, H query heads, Hkv KV heads (H % Hkv == 0, G = H / Hkv),
- *   L sequence length, d head dim (64 or 128), keep = |S_h| per query head, W score
+ *   L sequence length, d head dim (64 or 128), keep = |S| positions per subset, W score
  *   window, n_sink sink tokens, dtype of q/k/v/residual/out and of the compact
  *   tensors, scale of the logits (0 means 1/sqrt(d)).
  * Grouped-query map: query head h reads KV head g(h) = h / G.
+ * Subsets (tsa_desc.subsets): TSA_SUBSETS_PER_HEAD (the pages' method: every query head
+ *   keeps its own subset S_h, R = H subsets) or TSA_SUBSETS_PER_KV_HEAD (an extension of
+ *   this library, not from the pages: the G query heads of KV head g share one subset
+ *   S_g, chosen by the same rule on the sum of their G score rows, R = Hkv subsets).  Query
+ *   head h uses subset r(h) = h / (H / R).
  * Layouts (contiguous, row-major, element strides implied by the sizes):
  *   q, residual, out, o        [B][L][H][d]      (dtype)
  *   k, v                        [B][L][Hkv][d]    (dtype)
- *   scores                      [B][H][L]         (fp32)
- *   idx                         [B][H][keep]      (int32, strictly ascending per head)
- *   qh, kh, vh, oh              [B][H][keep][d]   (dtype; compact per-head tensors)
+ *   scores                      [B][H][L]         (fp32, always per query head)
+ *   idx                         [B][R][keep]      (int32, strictly ascending per subset)
+ *   qh, oh                      [B][H][keep][d]   (dtype; compact per-query-head tensors)
+ *   kh, vh                      [B][R][keep][d]   (dtype; compact K/V rows of each subset,
+ *                                                  read from KV head g(h) of its heads)
  * Memory and ownership: every pointer is a device pointer allocated by the caller and
  *   aligned to 16 bytes; the library allocates and frees nothing, keeps no pointer
  *   after a call returns, and holds no mutable global state.  Scratch space comes from
@@ -45,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 1
+#define TSA_ABI_VERSION 2
 #define TSA_MAX_W 64 /* largest score window the scoring kernel holds in registers */
 
 typedef enum {
@@ -58,21 +65,25 @@ typedef enum {
   TSA_ERR_WORKSPACE = 6, /* ws_bytes smaller than tsa_workspace_size, or ws NULL when needed */
   TSA_ERR_ALIAS = 7,     /* an output overlaps an input it must not overlap */
   TSA_ERR_LAUNCH = 8,    /* a kernel launch failed */
-  TSA_ERR_ARG = 9        /* an enum argument (op) out of range, or scale not finite / negative */
+  TSA_ERR_ARG = 9        /* an enum argument (op, subsets) out of range, or scale not finite / negative */
 } tsa_status;
 
 typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
+
+/* Who shares a token subset (see "Subsets" above). */
+typedef enum { TSA_SUBSETS_PER_HEAD = 0, TSA_SUBSETS_PER_KV_HEAD = 1 } tsa_subsets;
 
 /* Which call a workspace is sized for. */
 typedef enum { TSA_OP_SCORE = 0, TSA_OP_SELECT = 1, TSA_OP_SCATTER = 2, TSA_OP_FORWARD = 3 } tsa_op;
 
 typedef struct {
   int32_t B, H, Hkv, L, d;
-  int32_t keep;   /* |S_h|, the number of positions each query head keeps */
+  int32_t keep;   /* |S|, the number of positions each subset keeps */
   int32_t W;      /* score window: the last min(W, L) query positions score the keys */
   int32_t n_sink; /* positions [0, n_sink) are always kept */
   int32_t dtype;  /* tsa_dtype */
   float scale;    /* logit scale; 0 selects 1/sqrt(d) */
+  int32_t subsets; /* tsa_subsets */
 } tsa_desc;
 
 /* Returns TSA_ABI_VERSION. */
@@ -82,7 +93,8 @@ int tsa_abi_version(void);
 const char* tsa_status_str(int status);
 
 /* Host-only validation of a descriptor (no HIP call).  Forced set
- * F = [0, min(n_sink, L)) U [L - min(W, L), L); keep must satisfy |F| <= keep <= L. */
+ * F = [0, min(n_sink, L)) U [L - min(W, L), L); keep must satisfy |F| <= keep <= L;
+ * subsets must be a tsa_subsets value (else TSA_ERR_ARG). */
 tsa_status tsa_check(const tsa_desc* desc);
 
 /* Host-only: bytes of workspace the call `op` needs for `desc` (written to *bytes). */
@@ -99,32 +111,36 @@ tsa_status tsa_score(const tsa_desc* desc, const void* q, const void* k, float* 
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Top-K selection (skill page, Step 1, selection of the top-scoring tokens; the paper
- * page's Figure 3 per-head subset S_h).  Per (b, h): S_h = F plus the keep - |F|
- * non-forced positions with the largest scores, equal scores going to the lower
- * position; written ascending to idx[b][h][0..keep).  Scores must be >= 0 (as
- * tsa_score produces).  In: scores.  Out: idx.  Workspace: TSA_OP_SELECT (0 bytes:
- * ws may be NULL). */
+ * page's Figure 3 per-head subset S_h).  Per (b, r): S = F plus the keep - |F|
+ * non-forced positions with the largest subset scores, equal scores going to the lower
+ * position; written ascending to idx[b][r][0..keep).  The subset score is the head's
+ * score row (per head) or, per KV head, the fp32 sum of the G rows of its query heads
+ * taken in ascending head order.  Scores must be >= 0 (as tsa_score produces).  In:
+ * scores [B][H][L].  Out: idx [B][R][keep].  Workspace: TSA_OP_SELECT (0 bytes per head,
+ * ws may then be NULL; B*Hkv*L*4 bytes of summed scores per KV head). */
 tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Gather-compression (skill page, Step 2, gathering the selected tokens; Figure 3,
- * stage 1):  qh[b][h][t] = q[b][idx[b][h][t]][h],  kh[b][h][t] = k[b][idx][g(h)],
- * vh[b][h][t] = v[b][idx][g(h)].  Bit-exact copies.  idx entries must lie in [0, L).
- * The outputs must not overlap the inputs. */
+ * stage 1):  qh[b][h][t] = q[b][idx[b][r(h)][t]][h]; for each subset r, with g the KV
+ * head of its query heads, kh[b][r][t] = k[b][idx[b][r][t]][g] and vh likewise.
+ * Bit-exact copies.  idx entries must lie in [0, L).  The outputs must not overlap the
+ * inputs or one another. */
 tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v,
                           const int32_t* idx, void* qh, void* kh, void* vh, void* stream);
 
 /* Dense causal attention on the compact rows (skill page, Step 3; Figure 3, stage 2):
- *   oh[b][h][t] = sum over u <= t of softmax_u( scale * <qh[b][h][t], kh[b][h][u]> ) vh[b][h][u],
- * fp32 accumulation and online softmax, result rounded once to dtype.  Because S_h is
- * ascending, the causal mask on compact rows equals the mask on original positions.
- * oh must not overlap qh, kh or vh. */
+ *   oh[b][h][t] = sum over u <= t of
+ *                 softmax_u( scale * <qh[b][h][t], kh[b][r(h)][u]> ) vh[b][r(h)][u],
+ * fp32 accumulation and online softmax, result rounded once to dtype.  Because every
+ * subset is ascending, the causal mask on compact rows equals the mask on original
+ * positions.  oh must not overlap qh, kh or vh. */
 tsa_status tsa_attn(const tsa_desc* desc, const void* qh, const void* kh, const void* vh,
                     void* oh, void* stream);
 
 /* Scatter-decompression plus residual (skill page, Step 2, scattering back to the full
  * sequence; Figure 3: scatter into the full layout, then add the residual):
- *   out[b][p][h] = residual[b][p][h] + oh[b][h][t]   if p = idx[b][h][t],
+ *   out[b][p][h] = residual[b][p][h] + oh[b][h][t]   if p = idx[b][r(h)][t],
  *   out[b][p][h] = residual[b][p][h]                 (bit-exact) otherwise.
  * The sum is formed in fp32 and rounded once (round to nearest even).  out == residual
  * (exactly the same pointer) updates in place and touches only the kept rows; any other

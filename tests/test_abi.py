@@ -25,7 +25,7 @@ def test_header_declares_and_library_exports_every_entry_point():
     assert declared == EXPECTED
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tsa_abi_version() == 1
+    assert L.tsa_abi_version() == 2
     assert L.tsa_status_str(7) and L.tsa_status_str(1234) == b"unknown status"
 
 

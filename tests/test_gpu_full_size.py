@@ -123,3 +123,50 @@ def test_full_planted_recall_and_distinct_heads():
           f"{np.mean(jac):.3f} max {max(jac):.3f}")
     assert min(recalls) >= 0.99
     assert max(jac) < 0.5
+
+
+def test_full_per_kv_head_L128k():
+    # Subsets shared per KV head at L = 131072, keep 0.25, through tsa_forward (bf16 fused).
+    w, x = _inputs("bf16_L128k_r0.25")
+    dt = torch.bfloat16
+    q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
+    out, sg, ig = tsa.forward(q, k, v, r, w.keep, w.W, w.n_sink, return_scores=True, per_kv_head=True)
+    torch.cuda.synchronize()
+    B, L, H, d = x["q"].shape
+    G = H // w.Hkv
+    scale = 1.0 / np.sqrt(d)
+    idx_all = ig.cpu().numpy().astype(np.int64)
+    assert idx_all.shape == (B, w.Hkv, w.keep)
+    assert np.all(np.diff(idx_all, axis=-1) > 0)
+    F = oracle.forced_positions(L, w.W, w.n_sink)
+    assert all(np.all(np.isin(F, idx_all[b, g])) for b in range(B) for g in range(w.Hkv))
+    sel = torch.zeros(B, w.Hkv, L, dtype=torch.bool, device="cuda")
+    sel.scatter_(2, ig.long(), True)
+    sel = sel.repeat_interleave(G, dim=1).permute(0, 2, 1)       # [B, L, H]: head h uses subset h // G
+    assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16))
+    s32 = sg.cpu().numpy()
+    rng = np.random.default_rng(2)
+    worst_s, worst_out, n_diff = 0.0, 0.0, 0
+    for b, g in [(0, 1), (0, 6)]:
+        heads = range(g * G, (g + 1) * G)
+        kg = x["k"][b, :, g, :].astype(np.float64)
+        vg = x["v"][b, :, g, :].astype(np.float64)
+        s_or = np.stack([oracle.score_head(x["q"][b, :, h, :].astype(np.float64), kg, w.W, scale) for h in heads])
+        worst_s = max(worst_s, rel_err(s32[b, g * G:(g + 1) * G].astype(np.float64), s_or))
+        idx = idx_all[b, g]
+        # select bit-exact on the GPU's own fp32 scores, summed in fp32 in ascending head order
+        assert np.array_equal(idx, oracle.select(s32[b:b + 1, g * G:(g + 1) * G], w.keep, w.W, w.n_sink,
+                                                 kv_heads=1)[0, 0])
+        n_diff += check_selection(oracle.group_scores(s_or[None], 1), idx[None, None], w.keep, w.W, w.n_sink)
+        for h in (heads[0], heads[-1]):
+            qh = x["q"][b, :, h, :].astype(np.float64)
+            rows = np.unique(np.concatenate([[0, w.keep - 1], rng.integers(0, w.keep, 6)]))
+            o_rows = oracle.attend_rows(qh[idx], kg[idx], vg[idx], rows, scale)
+            pos = idx[rows]
+            got = out[b, torch.from_numpy(pos).cuda(), h, :].float().cpu().numpy().astype(np.float64)
+            want = x["r"][b, pos, h, :].astype(np.float64) + o_rows
+            worst_out = max(worst_out, float((np.abs(got - want) - half_ulp(got, w.dtype)).max()))
+    print(f"{w.name} per KV head: score rel err {worst_s:.2e}, out excess {worst_out:.2e}, "
+          f"subset differences {n_diff}")
+    assert worst_s <= 1e-5
+    assert worst_out <= TOL[w.dtype]

@@ -175,20 +175,24 @@ def test_score_zero_query_exact_ties():
 
 # ---- end to end ---------------------------------------------------------------------------
 
-def _end_to_end(x, dt, keep, W, ns, in_place=False):
+def _end_to_end(x, dt, keep, W, ns, in_place=False, per_kv_head=False):
     q, k, v, r = (dev(x[n], dt) for n in "qkvr")
+    Hkv = x["k"].shape[2]
+    kvh = Hkv if per_kv_head else None
     if in_place:
         out = r.clone()
-        _, sg, ig = tsa.forward(q, k, v, out, keep, W, ns, out=out, return_scores=True)
+        _, sg, ig = tsa.forward(q, k, v, out, keep, W, ns, out=out, return_scores=True, per_kv_head=per_kv_head)
     else:
-        out, sg, ig = tsa.forward(q, k, v, r, keep, W, ns, return_scores=True)
-    s_gpu = sg.cpu().numpy().astype(np.float64)
+        out, sg, ig = tsa.forward(q, k, v, r, keep, W, ns, return_scores=True, per_kv_head=per_kv_head)
+    s32 = sg.cpu().numpy()
+    s_gpu = s32.astype(np.float64)
     idx = ig.cpu().numpy().astype(np.int64)
     s_or = oracle.score(x["q"], x["k"], W)
     print(f"score max rel err {rel_err(s_gpu, s_or):.3e}")
     assert rel_err(s_gpu, s_or) <= 1e-5
-    assert np.array_equal(idx, oracle.select(s_gpu, keep, W, ns))   # select stage bit-exact on its own input
-    n_diff = check_selection(s_or, idx, keep, W, ns)
+    # select stage bit-exact on its own input (per KV head: summed in fp32, as the kernel does)
+    assert np.array_equal(idx, oracle.select(s32, keep, W, ns, kvh))
+    n_diff = check_selection(oracle.group_scores(s_or, Hkv) if per_kv_head else s_or, idx, keep, W, ns)
     qh, kh, vh = oracle.gather(x["q"], x["k"], x["v"], idx)
     oh_or = oracle.attend(qh, kh, vh)
     # Attention stage on the GPU's own subset: the 1e-4 / 2e-2 bar.
@@ -203,13 +207,15 @@ def _end_to_end(x, dt, keep, W, ns, in_place=False):
     got = host(out)
     B, L, H, _ = x["q"].shape
     sel = np.zeros((B, L, H), dtype=bool)
+    SG = H // idx.shape[1]
     for b in range(B):
         for h in range(H):
-            sel[b, idx[b, h], h] = True
+            sel[b, idx[b, h // SG], h] = True
     assert np.array_equal(got[~sel], x["r"][~sel].astype(np.float64))
     excess = np.abs(got[sel] - want[sel]) - half_ulp(got[sel], dt)
     err = float(np.max(np.abs(got[sel] - round_to(want[sel], dt))))
-    print(f"end-to-end {dt}: attn err {att_err:.3e}, out err vs once-rounded oracle {err:.3e}, "
+    print(f"end-to-end {dt}{' per KV head' if per_kv_head else ''}: attn err {att_err:.3e}, "
+          f"out err vs once-rounded oracle {err:.3e}, "
           f"excess over half-ulp {excess.max():.3e}, subset differences {n_diff}")
     assert excess.max() <= TOL[dt]
 
@@ -310,3 +316,90 @@ def test_deterministic():
     b = tsa.forward(q, k, v, r, 700, 64, 4, return_scores=True)
     for ta, tb in zip(a, b):
         assert torch.equal(ta, tb)
+
+
+# ---- token subsets shared per KV head ----------------------------------------------------
+
+@pytest.mark.parametrize("B,H,Hkv,L,keep,W,ns,ties", [
+    (1, 8, 2, 1000, 137, 5, 3, False),
+    (2, 4, 1, 777, 300, 64, 4, True),
+    (1, 6, 3, 513, 68, 64, 4, False),        # keep = |F|
+    (1, 4, 4, 300, 100, 8, 2, True),         # one query head per KV head
+    (1, 32, 8, 131072, 32768, 64, 4, True),
+])
+def test_select_per_kv_head_bitexact(B, H, Hkv, L, keep, W, ns, ties):
+    rng = np.random.default_rng(L + H)
+    s = rng.random((B, H, L)).astype(np.float32) * 0.01
+    if ties:
+        s = (np.round(s * 200) / 200).astype(np.float32)
+    s[..., :ns] = 0.0
+    idx = tsa.select(torch.from_numpy(s).cuda(), keep, W, ns, kv_heads=Hkv).cpu().numpy()
+    assert idx.shape == (B, Hkv, keep)
+    assert np.array_equal(idx, oracle.select(s, keep, W, ns, kv_heads=Hkv))
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp32", 64)])
+def test_gather_scatter_per_kv_head_bitexact(dt, d):
+    B, H, Hkv, L, keep = 2, 8, 2, 300, 77
+    x = workloads.small_random(B, H, Hkv, L, d, seed=23, dtype=dt)
+    rng = np.random.default_rng(6)
+    idx = np.stack([np.stack([np.sort(rng.choice(L, keep, replace=False)) for _ in range(Hkv)]) for _ in range(B)])
+    q, k, v, r = (dev(x[n], dt) for n in "qkvr")
+    ig = torch.from_numpy(idx.astype(np.int32)).cuda()
+    qh, kh, vh = tsa.gather_qkv(q, k, v, ig)
+    assert tuple(kh.shape) == (B, Hkv, keep, d)
+    wq, wk, wv = oracle.gather(x["q"], x["k"], x["v"], idx)
+    assert np.array_equal(host(qh), wq) and np.array_equal(host(kh), wk) and np.array_equal(host(vh), wv)
+    oh_vals = rng.standard_normal((B, H, keep, d)).astype(np.float32)
+    oh_vals = workloads.round_bf16(oh_vals) if dt == "bf16" else oh_vals
+    oh = dev(oh_vals, dt)
+    want = round_to(oracle.scatter_residual(oh_vals, idx, x["r"]), dt)
+    assert np.array_equal(host(tsa.scatter_residual(oh, ig, r)), want)
+    r2 = r.clone()
+    tsa.scatter_residual(oh, ig, r2, out=r2)
+    assert np.array_equal(host(r2), want)
+
+
+@pytest.mark.parametrize("dt,d,n", [("bf16", 128, 300), ("bf16", 128, 1000), ("bf16", 64, 257), ("fp32", 128, 200)])
+def test_attn_per_kv_head(dt, d, n):
+    B, H, Hkv = 1, 8, 2
+    rng = np.random.default_rng(n + d + 1)
+    qh = rng.standard_normal((B, H, n, d)).astype(np.float32)
+    kh, vh = (rng.standard_normal((B, Hkv, n, d)).astype(np.float32) for _ in range(2))
+    if dt == "bf16":
+        qh, kh, vh = (workloads.round_bf16(t) for t in (qh, kh, vh))
+    oh = tsa.attn(dev(qh, dt), dev(kh, dt), dev(vh, dt))
+    err = np.max(np.abs(host(oh) - oracle.attend(qh, kh, vh)))
+    print(f"attn per KV head {dt} d={d} n={n}: max abs err {err:.3e}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,keep,W,ns,in_place", [
+    (1, 8, 2, 1000, 128, 400, 64, 4, False),
+    (2, 8, 4, 700, 128, 300, 16, 2, True),
+    (1, 4, 1, 513, 64, 200, 64, 4, False),
+])
+def test_forward_bf16_per_kv_head(B, H, Hkv, L, d, keep, W, ns, in_place):
+    x = workloads.small_random(B, H, Hkv, L, d, seed=31, dtype="bf16")
+    _end_to_end(x, "bf16", keep, W, ns, in_place=in_place, per_kv_head=True)
+
+
+def test_forward_fp32_per_kv_head():
+    x = workloads.small_random(1, 4, 2, 512, 64, seed=32, dtype="fp32")
+    _end_to_end(x, "fp32", 256, 32, 4, per_kv_head=True)
+    _end_to_end(x, "fp32", 256, 32, 4, in_place=True, per_kv_head=True)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_fused_equals_staged_per_kv_head(in_place):
+    x = workloads.small_random(2, 8, 2, 1234, 128, seed=18, dtype="bf16")
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    if in_place:
+        out = r.clone()
+        _, s_f, idx = tsa.forward(q, k, v, out, 500, 64, 4, out=out, return_scores=True, per_kv_head=True)
+    else:
+        out, s_f, idx = tsa.forward(q, k, v, r, 500, 64, 4, return_scores=True, per_kv_head=True)
+    assert tuple(idx.shape) == (2, 2, 500)
+    staged = tsa.scatter_residual(tsa.attn(*tsa.gather_qkv(q, k, v, idx)), idx, r)
+    assert torch.equal(out, staged)
+    assert torch.equal(tsa.select(s_f, 500, 64, 4, kv_heads=2), idx)

@@ -6,8 +6,10 @@ points (``tsa_score`` ... ``tsa_dense_attn``) take every buffer explicitly; the
 lower-case helpers below them allocate outputs and workspace with torch and call them.
 
 Layouts (contiguous): q, residual, out ``[B, L, H, d]``; k, v ``[B, L, Hkv, d]``;
-scores ``[B, H, L]`` fp32; idx ``[B, H, keep]`` int32 ascending; compact tensors
-``[B, H, keep, d]``.  dtypes: float32 or bfloat16, head dim 64 or 128.
+scores ``[B, H, L]`` fp32; idx ``[B, R, keep]`` int32 ascending; compact qh, oh
+``[B, H, keep, d]`` and kh, vh ``[B, R, keep, d]``, where R = H (one token subset per
+query head) or R = Hkv (``per_kv_head=True``: the query heads of a KV head share one
+subset chosen on their summed scores).  dtypes: float32 or bfloat16, head dim 64 or 128.
 
 The library must have been built (``token_sparse_attention_head_amd/build.py``);
 importing this package without it raises ImportError: there is no fallback path.
@@ -27,6 +29,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tsa.h")
 TSA_OK = 0
 TSA_F32, TSA_BF16 = 0, 1
 TSA_OP_SCORE, TSA_OP_SELECT, TSA_OP_SCATTER, TSA_OP_FORWARD = 0, 1, 2, 3
+TSA_SUBSETS_PER_HEAD, TSA_SUBSETS_PER_KV_HEAD = 0, 1
+ABI_VERSION = 2   # TSA_ABI_VERSION of include/tsa.h that this binding's TsaDesc matches
 STATUS_NAMES = {0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_SHAPE", 3: "TSA_ERR_BUDGET", 4: "TSA_ERR_DTYPE",
                 5: "TSA_ERR_ALIGN", 6: "TSA_ERR_WORKSPACE", 7: "TSA_ERR_ALIAS", 8: "TSA_ERR_LAUNCH", 9: "TSA_ERR_ARG"}
 
@@ -34,7 +38,7 @@ STATUS_NAMES = {0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_SHAPE", 3: "TSA_ERR_
 class TsaDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("keep", ctypes.c_int32), ("W", ctypes.c_int32), ("n_sink", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("subsets", ctypes.c_int32)]
 
     def __repr__(self):
         return "TsaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -76,6 +80,9 @@ def lib():
             fn = getattr(h, name)
             fn.argtypes = args
             fn.restype = res
+        if h.tsa_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {h.tsa_abi_version()}, the binding expects {ABI_VERSION}; "
+                              "rebuild it with token_sparse_attention_head_amd/build.py")
         _LIB = h
     return _LIB
 
@@ -88,9 +95,10 @@ def header_functions() -> list[str]:
 
 # ---- descriptors and marshalling ------------------------------------------------------
 
-def make_desc(B, H, Hkv, L, d, keep, W, n_sink, dtype, scale: float = 0.0) -> TsaDesc:
+def make_desc(B, H, Hkv, L, d, keep, W, n_sink, dtype, scale: float = 0.0, subsets: int = 0) -> TsaDesc:
     code = {torch.float32: TSA_F32, torch.bfloat16: TSA_BF16}.get(dtype, dtype)
-    return TsaDesc(int(B), int(H), int(Hkv), int(L), int(d), int(keep), int(W), int(n_sink), int(code), float(scale))
+    return TsaDesc(int(B), int(H), int(Hkv), int(L), int(d), int(keep), int(W), int(n_sink), int(code), float(scale),
+                   int(subsets))
 
 
 def _ptr(t) -> int | None:
@@ -177,10 +185,11 @@ def _check_io(q, k, v=None):
         raise ValueError("q must be [B, L, H, d] and k, v [B, L, Hkv, d]")
 
 
-def desc_for(q, k, keep, W=64, n_sink=4, scale=0.0) -> TsaDesc:
+def desc_for(q, k, keep, W=64, n_sink=4, scale=0.0, per_kv_head=False) -> TsaDesc:
     B, L, H, d = q.shape
     keep = min(int(keep), L)   # a budget larger than the sequence keeps everything
-    return make_desc(B, H, k.shape[2], L, d, keep, W, n_sink, q.dtype, scale)
+    return make_desc(B, H, k.shape[2], L, d, keep, W, n_sink, q.dtype, scale,
+                     TSA_SUBSETS_PER_KV_HEAD if per_kv_head else TSA_SUBSETS_PER_HEAD)
 
 
 def _workspace(desc, op, device):
@@ -197,32 +206,43 @@ def score(q, k, W=64, scale=0.0):
     return scores
 
 
-def select(scores, keep, W=64, n_sink=4):
-    """idx [B, H, keep] (int32, ascending) from scores [B, H, L]."""
+def select(scores, keep, W=64, n_sink=4, kv_heads=None):
+    """idx [B, R, keep] (int32, ascending) from scores [B, H, L]: one subset per query head
+    (R = H), or with kv_heads=Hkv one per KV head on the summed scores of its heads."""
     if not scores.is_cuda or scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous float32 GPU tensor")
     B, H, L = scores.shape
     keep = min(int(keep), L)
-    desc = make_desc(B, H, H, L, 128, keep, W, n_sink, TSA_F32)
-    idx = torch.empty(B, H, keep, dtype=torch.int32, device=scores.device)
-    tsa_select(desc, scores, idx)
+    R = H if kv_heads is None else int(kv_heads)
+    desc = make_desc(B, H, R, L, 128, keep, W, n_sink, TSA_F32, 0.0,
+                     TSA_SUBSETS_PER_HEAD if kv_heads is None else TSA_SUBSETS_PER_KV_HEAD)
+    idx = torch.empty(B, R, keep, dtype=torch.int32, device=scores.device)
+    ws = _workspace(desc, TSA_OP_SELECT, scores.device)
+    tsa_select(desc, scores, idx, ws, ws.numel())
     return idx
 
 
 def gather_qkv(q, k, v, idx):
+    """qh [B, H, keep, d], kh, vh [B, R, keep, d] from idx [B, R, keep] (R = H or Hkv)."""
     _check_io(q, k, v)
     B, L, H, d = q.shape
-    desc = desc_for(q, k, idx.shape[2], W=1, n_sink=0)
-    shape = (B, H, idx.shape[2], d)
-    qh, kh, vh = (torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    R = idx.shape[1]
+    if R not in (H, k.shape[2]) or idx.shape[0] != B:
+        raise ValueError(f"idx must be [B, H, keep] or [B, Hkv, keep]; got {tuple(idx.shape)}")
+    desc = desc_for(q, k, idx.shape[2], W=1, n_sink=0, per_kv_head=R != H)
+    qh = torch.empty(B, H, idx.shape[2], d, dtype=q.dtype, device=q.device)
+    kh, vh = (torch.empty(B, R, idx.shape[2], d, dtype=q.dtype, device=q.device) for _ in range(2))
     tsa_gather_qkv(desc, q, k, v, idx, qh, kh, vh)
     return qh, kh, vh
 
 
 def attn(qh, kh, vh, scale=0.0):
-    """Causal attention over the compact rows of every (batch, head): [B, H, keep, d]."""
+    """Causal attention over the compact rows of every (batch, head): qh [B, H, keep, d],
+    kh, vh [B, R, keep, d] (query head h uses row block h / (H / R))."""
     B, H, n, d = qh.shape
-    desc = make_desc(B, H, H, n, d, n, 1, 0, qh.dtype, scale)
+    R = kh.shape[1]
+    desc = make_desc(B, H, R, n, d, n, 1, 0, qh.dtype, scale,
+                     TSA_SUBSETS_PER_KV_HEAD if R != H else TSA_SUBSETS_PER_HEAD)
     oh = torch.empty_like(qh)
     tsa_attn(desc, qh, kh, vh, oh)
     return oh
@@ -231,7 +251,9 @@ def attn(qh, kh, vh, scale=0.0):
 def scatter_residual(oh, idx, residual, out=None):
     """out = residual + scatter(oh at idx); out=residual updates in place."""
     B, L, H, d = residual.shape
-    desc = make_desc(B, H, H, L, d, idx.shape[2], 1, 0, residual.dtype)
+    R = idx.shape[1]
+    desc = make_desc(B, H, R, L, d, idx.shape[2], 1, 0, residual.dtype, 0.0,
+                     TSA_SUBSETS_PER_KV_HEAD if R != H else TSA_SUBSETS_PER_HEAD)
     if out is None:
         out = torch.empty_like(residual)
     ws = None if out.data_ptr() == residual.data_ptr() else _workspace(desc, TSA_OP_SCATTER, residual.device)
@@ -239,10 +261,12 @@ def scatter_residual(oh, idx, residual, out=None):
     return out
 
 
-def forward(q, k, v, residual, keep, W=64, n_sink=4, scale=0.0, out=None, return_scores=False, ws=None):
-    """One token-sparse attention layer: returns out (and scores, idx when asked)."""
+def forward(q, k, v, residual, keep, W=64, n_sink=4, scale=0.0, out=None, return_scores=False, ws=None,
+            per_kv_head=False):
+    """One token-sparse attention layer: returns out (and scores [B, H, L], idx [B, R, keep]
+    when asked)."""
     _check_io(q, k, v)
-    desc = desc_for(q, k, keep, W, n_sink, scale)
+    desc = desc_for(q, k, keep, W, n_sink, scale, per_kv_head)
     if out is None:
         out = torch.empty_like(residual)
     if ws is None:
@@ -251,7 +275,7 @@ def forward(q, k, v, residual, keep, W=64, n_sink=4, scale=0.0, out=None, return
     if return_scores:
         B, L, H, _ = q.shape
         scores = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
-        idx = torch.empty(B, H, desc.keep, dtype=torch.int32, device=q.device)
+        idx = torch.empty(B, k.shape[2] if per_kv_head else H, desc.keep, dtype=torch.int32, device=q.device)
     tsa_forward(desc, q, k, v, residual, out, scores, idx, ws)
     return (out, scores, idx) if return_scores else out
 

@@ -39,6 +39,7 @@ tsa_status check_shape(const tsa_desc* d) {
   if (d->H % d->Hkv != 0) return TSA_ERR_SHAPE;
   if (d->d != 64 && d->d != 128) return TSA_ERR_SHAPE;
   if (!std::isfinite(d->scale) || d->scale < 0.f) return TSA_ERR_ARG;
+  if (d->subsets != TSA_SUBSETS_PER_HEAD && d->subsets != TSA_SUBSETS_PER_KV_HEAD) return TSA_ERR_ARG;
   // Index limits of the launch grids (grid.y = B*H, 32-bit thread indices per batch entry).
   if ((int64_t)d->B * d->H > 65535) return TSA_ERR_SHAPE;
   const int64_t chunks_per_row = (int64_t)d->d * elem_bytes(*d) / 16;
@@ -92,9 +93,10 @@ tsa_status after_launch(hipError_t e, hipStream_t s) {
     if (st_ != TSA_OK) return st_;       \
   } while (0)
 
-// Byte sizes of the tensors of a descriptor.
+// Byte sizes of the tensors of a descriptor (idx, inv and the compact K/V have one row
+// per subset: H of them per head, Hkv per KV head; gsum holds the summed score rows).
 struct Sizes {
-  size_t q, kv, scores, idx, compact, inv, part, stat;
+  size_t q, kv, scores, idx, compact, kvc, inv, gsum, part, stat;
 };
 
 Sizes sizes_of(const tsa_desc& d) {
@@ -103,9 +105,12 @@ Sizes sizes_of(const tsa_desc& d) {
   z.q = (size_t)d.B * d.L * d.H * d.d * e;
   z.kv = (size_t)d.B * d.L * d.Hkv * d.d * e;
   z.scores = (size_t)d.B * d.H * d.L * 4;
-  z.idx = (size_t)d.B * d.H * d.keep * 4;
+  const int R = tsa::subset_rows(d);
+  z.idx = (size_t)d.B * R * d.keep * 4;
   z.compact = (size_t)d.B * d.H * d.keep * d.d * e;
-  z.inv = (size_t)d.B * d.H * d.L * 4;
+  z.kvc = (size_t)d.B * R * d.keep * d.d * e;
+  z.inv = (size_t)d.B * R * d.L * 4;
+  z.gsum = R < d.H ? (size_t)d.B * R * d.L * 4 : 0;
   int chunk = 32, nchunk = 1;
   if (d.L > 0) tsa::score_chunking(d, chunk, nchunk);
   z.part = (size_t)d.B * d.H * nchunk * window(d) * 8;
@@ -117,22 +122,24 @@ Sizes sizes_of(const tsa_desc& d) {
 // bf16 forward is fused (attention reads the rows through idx and writes residual + O), so
 // it needs no compact tensors; the fp32 forward runs the stages one after the other.
 struct FwdLayout {
-  size_t scores, idx, inv, part, stat, qh, kh, vh, oh, total;
+  size_t scores, idx, inv, gsum, part, stat, qh, kh, vh, oh, total;
 };
 
 FwdLayout fwd_layout(const tsa_desc& d) {
   const Sizes z = sizes_of(d);
   const size_t comp = fused_forward(d) ? 0 : round_up(z.compact);
+  const size_t kvc = fused_forward(d) ? 0 : round_up(z.kvc);
   FwdLayout f;
   size_t o = 0;
   f.scores = o; o += round_up(z.scores);
   f.idx = o; o += round_up(z.idx);
   f.inv = o; o += round_up(z.inv);
+  f.gsum = o; o += round_up(z.gsum);
   f.part = o; o += round_up(z.part);
   f.stat = o; o += round_up(z.stat);
   f.qh = o; o += comp;
-  f.kh = o; o += comp;
-  f.vh = o; o += comp;
+  f.kh = o; o += kvc;
+  f.vh = o; o += kvc;
   f.oh = o; o += comp;
   f.total = o;
   return f;
@@ -173,7 +180,7 @@ tsa_status tsa_workspace_size(const tsa_desc* desc, int op, size_t* bytes) {
   const Sizes z = sizes_of(*desc);
   switch (op) {
     case TSA_OP_SCORE: *bytes = round_up(z.part) + round_up(z.stat); break;
-    case TSA_OP_SELECT: *bytes = 0; break;
+    case TSA_OP_SELECT: *bytes = round_up(z.gsum); break;
     case TSA_OP_SCATTER: *bytes = round_up(z.inv); break;
     case TSA_OP_FORWARD: *bytes = fwd_layout(*desc).total; break;
     default: return TSA_ERR_ARG;
@@ -202,17 +209,20 @@ tsa_status tsa_score(const tsa_desc* desc, const void* q, const void* k, float* 
 
 tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx, void* ws, size_t ws_bytes,
                       void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   TSA_TRY(check_full(desc));
   const tsa_desc& d = *desc;
   if (empty_problem(d)) return TSA_OK;
   if (!scores || !idx) return TSA_ERR_NULL;
-  if (!aligned(scores) || !aligned(idx)) return TSA_ERR_ALIGN;
+  if (!aligned(scores) || !aligned(idx) || !aligned(ws)) return TSA_ERR_ALIGN;
   const Sizes z = sizes_of(d);
   if (overlap({scores, z.scores}, {idx, z.idx})) return TSA_ERR_ALIAS;
+  const size_t need = round_up(z.gsum);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+    if (overlap({ws, need}, {scores, z.scores}) || overlap({ws, need}, {idx, z.idx})) return TSA_ERR_ALIAS;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(tsa::launch_select(d, scores, idx, nullptr, s), s);
+  return after_launch(tsa::launch_select(d, scores, idx, nullptr, static_cast<float*>(ws), s), s);
 }
 
 tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -224,7 +234,7 @@ tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, co
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(idx) || !aligned(qh) || !aligned(kh) || !aligned(vh))
     return TSA_ERR_ALIGN;
   const Sizes z = sizes_of(d);
-  const Range outs[3] = {{qh, z.compact}, {kh, z.compact}, {vh, z.compact}};
+  const Range outs[3] = {{qh, z.compact}, {kh, z.kvc}, {vh, z.kvc}};
   const Range ins[4] = {{q, z.q}, {k, z.kv}, {v, z.kv}, {idx, z.idx}};
   for (const Range& o : outs)
     for (const Range& i : ins)
@@ -242,7 +252,7 @@ tsa_status tsa_attn(const tsa_desc* desc, const void* qh, const void* kh, const 
   if (!aligned(qh) || !aligned(kh) || !aligned(vh) || !aligned(oh)) return TSA_ERR_ALIGN;
   const Sizes z = sizes_of(d);
   const Range ro{oh, z.compact};
-  if (overlap(ro, {qh, z.compact}) || overlap(ro, {kh, z.compact}) || overlap(ro, {vh, z.compact}))
+  if (overlap(ro, {qh, z.compact}) || overlap(ro, {kh, z.kvc}) || overlap(ro, {vh, z.kvc}))
     return TSA_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(launch_attn_compact(d, qh, kh, vh, oh, s), s);
@@ -304,10 +314,10 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   void* oh = at<char>(ws, f.oh);
   const bool in_place = out == residual;
   TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
-  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, s), s));
+  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, at<float>(ws, f.gsum), s), s));
   if (fused_forward(d)) {
-    // Rows no head keeps are the residual (copied out of place, untouched in place); the
-    // attention epilogue writes residual + O into the kept rows.
+    // Rows a head does not keep are the residual (copied out of place, untouched in place);
+    // the attention epilogue writes residual + O into the kept rows.
     if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
     if (d.keep == 0) return TSA_OK;
     return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, residual, out, s), s);

@@ -52,7 +52,8 @@ struct AttnParams {
   int kv_div;              // KV head of query head h is h / kv_div
   int BH, ntiles;
   float c;                 // logit scale * log2(e)
-  const int32_t* idx;      // fused forward: [B][H][n] positions of each head's rows
+  const int32_t* idx;      // fused forward: [B][H / idx_div][n] positions of each subset's rows
+  int idx_div;             // query heads per subset: head h reads idx row b * (H / idx_div) + h / idx_div
   const void* res;         // fused forward: residual, same layout as o
 };
 
@@ -197,10 +198,7 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
 // row strides are compile-time constants.
 template <typename T, int D, int QB, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
-  if (!DENSE) {
-    p.q_r = p.k_r = p.o_r = D;
-    p.kv_div = 1;
-  }
+  if (!DENSE) p.q_r = p.k_r = p.o_r = D;
   __shared__ AttnLds<T, D> lds;
   constexpr int BM = NW * QB * 32;
   const int tid = threadIdx.x;
@@ -361,7 +359,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   // would be placed in scratch memory).
   const int n = p.n;
   const int64_t q_r = STRIDED ? p.q_r : D, k_r = STRIDED ? p.k_r : D, o_r = STRIDED ? p.o_r : D;
-  const int kv_div = STRIDED ? p.kv_div : 1;
+  const int kv_div = p.kv_div;
   const float c = p.c;
 
   const int tid = threadIdx.x;
@@ -389,7 +387,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h;
   __bf16* obase = reinterpret_cast<__bf16*>(p.o) + b * p.o_b + h * p.o_h;
-  const int32_t* idx_bh = FUSED ? p.idx + (int64_t)bh * p.n : nullptr;
+  const int32_t* idx_bh = FUSED ? p.idx + (b * (p.H / p.idx_div) + h / p.idx_div) * (int64_t)p.n : nullptr;
 
   const int q0 = tile * BM;
   const int wrow0 = q0 + wave * 32;
@@ -660,9 +658,9 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
   p.q = qh; p.k = kh; p.v = vh; p.o = oh;
   p.n = d.keep;
   p.H = d.H;
-  p.kv_div = 1;
+  p.kv_div = heads_per_subset(d);               // compact K/V rows are per subset
   p.q_r = d.d; p.q_h = (int64_t)d.keep * d.d; p.q_b = (int64_t)d.H * d.keep * d.d;
-  p.k_r = p.q_r; p.k_h = p.q_h; p.k_b = p.q_b;
+  p.k_r = p.q_r; p.k_h = p.q_h; p.k_b = (int64_t)subset_rows(d) * d.keep * d.d;
   p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
   p.c = attn_c(d);
   return dispatch_attn<false>(d, p, s);
@@ -673,6 +671,7 @@ hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, co
   if (d.dtype != TSA_BF16) return hipErrorInvalidValue;
   AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res;
+  p.idx_div = heads_per_subset(d);
   p.n = d.keep;
   p.H = d.H;
   p.kv_div = d.H / d.Hkv;

@@ -7,12 +7,19 @@
 
 namespace tsa {
 
+// Token subsets: R rows of idx (H per query head, Hkv per KV head) and the number of
+// query heads sharing one subset; query head h uses subset h / heads_per_subset.
+inline int subset_rows(const tsa_desc& d) { return d.subsets == TSA_SUBSETS_PER_KV_HEAD ? d.Hkv : d.H; }
+inline int heads_per_subset(const tsa_desc& d) { return d.H / subset_rows(d); }
+
 // Key chunking of the scoring passes (shared by the launcher and workspace sizing).
 void score_chunking(const tsa_desc& d, int& chunk, int& nchunk);
 
 hipError_t launch_score(const tsa_desc& d, const void* q, const void* k, float* scores, float2* part, float2* stat,
                         hipStream_t s);
-hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, hipStream_t s);
+// Per-KV-head subsets sum the score rows of each group into gsum ([B][Hkv][L], workspace).
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, float* gsum,
+                         hipStream_t s);
 hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              void* qh, void* kh, void* vh, hipStream_t s);
 hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh, const void* vh, void* oh,
@@ -20,7 +27,7 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
 // Fused forward attention (bf16): compact rows read through idx, out rows = residual + O.
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              const void* res, void* out, hipStream_t s);
-// Copies residual to out at the positions no head keeps (inverse map < 0), per head.
+// Copies residual to out at the positions a head does not keep (inverse map < 0).
 hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s);
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
                              hipStream_t s);

@@ -18,11 +18,14 @@ namespace tsa {
 
 namespace {
 
+// SG query heads share a subset (1 per head, G per KV head): head h reads idx row
+// b * (H / SG) + h / SG; the first head of each subset also writes the subset's K/V rows.
 template <int ROWB>
 __global__ __launch_bounds__(256) void gather_qkv_kernel(const char* __restrict__ q, const char* __restrict__ k,
                                                          const char* __restrict__ v, const int32_t* __restrict__ idx,
                                                          char* __restrict__ qh, char* __restrict__ kh,
-                                                         char* __restrict__ vh, int H, int G, int L, int keep) {
+                                                         char* __restrict__ vh, int H, int G, int SG, int L,
+                                                         int keep) {
   constexpr int CH = ROWB / 16;
   const int bh = blockIdx.y;                  // b * H + h
   const uint32_t e = blockIdx.x * 256u + threadIdx.x;
@@ -32,17 +35,16 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const char* __restrict_
   const int h = bh % H;
   const int64_t b = bh / H;
   const int Hkv = H / G;
-  const int64_t crow = (int64_t)bh * keep + t;
-  const int p = idx[crow];
+  const int64_t srow = (b * (H / SG) + h / SG) * keep + t;   // row of the subset
+  const int p = idx[srow];
   const int64_t qoff = ((b * L + p) * H + h) * ROWB + c * 16;
+  st16(qh + ((int64_t)bh * keep + t) * ROWB + c * 16, ld16(q + qoff));
+  if (h % SG != 0) return;
   const int64_t kvoff = ((b * L + p) * Hkv + h / G) * ROWB + c * 16;
-  const u32x4 a = ld16(q + qoff);
   const u32x4 kk = ld16(k + kvoff);
   const u32x4 vv = ld16(v + kvoff);
-  const int64_t o = crow * ROWB + c * 16;
-  st16(qh + o, a);
-  st16(kh + o, kk);
-  st16(vh + o, vv);
+  st16(kh + srow * ROWB + c * 16, kk);
+  st16(vh + srow * ROWB + c * 16, vv);
 }
 
 // 16 bytes of residual plus 16 bytes of attention output, summed in fp32, rounded once.
@@ -62,14 +64,14 @@ __device__ __forceinline__ u32x4 add_rows(u32x4 r, u32x4 o, tsa_dtype dt) {
   return out;
 }
 
-// Out-of-place: one pass over [B][L][H] rows in memory order.  inv[b][h][p] is the
-// compact row of position p in S_h, or -1.  SKIP_KEPT leaves kept rows untouched (the fused
+// Out-of-place: one pass over [B][L][H] rows in memory order.  inv[b][r][p] is the
+// compact row of position p in subset r, or -1; head h uses subset h / SG.  SKIP_KEPT leaves kept rows untouched (the fused
 // forward writes them from its attention epilogue).
 template <int ROWB, tsa_dtype DT, bool SKIP_KEPT = false>
 __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __restrict__ oh,
                                                                const int32_t* __restrict__ inv,
                                                                const char* __restrict__ res, char* __restrict__ out,
-                                                               int H, int L, int keep) {
+                                                               int H, int SG, int L, int keep) {
   constexpr int CH = ROWB / 16;
   const int64_t b = blockIdx.y;
   const uint32_t e = blockIdx.x * 256u + threadIdx.x;
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __res
   const int p = row / H;
   const int h = row % H;
   const int64_t off = ((b * L + p) * H + h) * ROWB + c * 16;
-  const int t = inv[(b * H + h) * L + p];
+  const int t = inv[(b * (H / SG) + h / SG) * L + p];
   if (SKIP_KEPT && t >= 0) return;
   const u32x4 r = ld16_nt(res + off);
   u32x4 o = r;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __res
 template <int ROWB, tsa_dtype DT>
 __global__ __launch_bounds__(256) void scatter_add_inplace_kernel(const char* __restrict__ oh,
                                                                   const int32_t* __restrict__ idx, char* out, int H,
-                                                                  int L, int keep) {
+                                                                  int SG, int L, int keep) {
   constexpr int CH = ROWB / 16;
   const int bh = blockIdx.y;
   const uint32_t e = blockIdx.x * 256u + threadIdx.x;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void scatter_add_inplace_kernel(const char* __
   const int h = bh % H;
   const int64_t b = bh / H;
   const int64_t crow = (int64_t)bh * keep + t;
-  const int p = idx[crow];
+  const int p = idx[(b * (H / SG) + h / SG) * keep + t];
   char* dst = out + ((b * L + p) * H + h) * ROWB + c * 16;
   st16(dst, add_rows(ld16(dst), ld16(oh + crow * ROWB + c * 16), DT));
 }
@@ -137,15 +139,15 @@ hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, co
   const dim3 grid(blocks_for((int64_t)d.keep * (rowb / 16)), d.B * d.H);
   TSA_ROWB_DISPATCH(rowb, gather_qkv_kernel<RB><<<grid, 256, 0, s>>>(
                               (const char*)q, (const char*)k, (const char*)v, idx, (char*)qh, (char*)kh, (char*)vh,
-                              d.H, d.H / d.Hkv, d.L, d.keep));
+                              d.H, d.H / d.Hkv, heads_per_subset(d), d.L, d.keep));
   return hipGetLastError();
 }
 
 hipError_t launch_build_inverse(const tsa_desc& d, const int32_t* idx, int32_t* inv, hipStream_t s) {
-  const int64_t n = (int64_t)d.B * d.H * d.L;
+  const int64_t n = (int64_t)d.B * subset_rows(d) * d.L;
   const unsigned fb = (unsigned)std::min<int64_t>(blocks_for(n), 4096);
   fill_kernel<<<fb, 256, 0, s>>>(inv, n, -1);
-  invert_kernel<<<dim3(blocks_for(d.keep), d.B * d.H), 256, 0, s>>>(idx, inv, d.L, d.keep);
+  invert_kernel<<<dim3(blocks_for(d.keep), d.B * subset_rows(d)), 256, 0, s>>>(idx, inv, d.L, d.keep);
   return hipGetLastError();
 }
 
@@ -155,10 +157,12 @@ hipError_t launch_scatter_residual(const tsa_desc& d, const void* oh, const int3
   const dim3 grid(blocks_for((int64_t)d.L * d.H * (rowb / 16)), d.B);
   if (d.dtype == TSA_BF16) {
     TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_BF16><<<grid, 256, 0, s>>>(
-                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
+                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, heads_per_subset(d), d.L,
+                                d.keep));
   } else {
     TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_F32><<<grid, 256, 0, s>>>(
-                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
+                                (const char*)oh, inv, (const char*)res, (char*)out, d.H, heads_per_subset(d), d.L,
+                                d.keep));
   }
   return hipGetLastError();
 }
@@ -167,7 +171,7 @@ hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const v
   const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
   const dim3 grid(blocks_for((int64_t)d.L * d.H * (rowb / 16)), d.B);
   TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_BF16, true><<<grid, 256, 0, s>>>(
-                              nullptr, inv, (const char*)res, (char*)out, d.H, d.L, d.keep));
+                              nullptr, inv, (const char*)res, (char*)out, d.H, heads_per_subset(d), d.L, d.keep));
   return hipGetLastError();
 }
 
@@ -176,10 +180,10 @@ hipError_t launch_scatter_inplace(const tsa_desc& d, const void* oh, const int32
   const dim3 grid(blocks_for((int64_t)d.keep * (rowb / 16)), d.B * d.H);
   if (d.dtype == TSA_BF16) {
     TSA_ROWB_DISPATCH(rowb, scatter_add_inplace_kernel<RB, TSA_BF16><<<grid, 256, 0, s>>>(
-                                (const char*)oh, idx, (char*)out, d.H, d.L, d.keep));
+                                (const char*)oh, idx, (char*)out, d.H, heads_per_subset(d), d.L, d.keep));
   } else {
     TSA_ROWB_DISPATCH(rowb, scatter_add_inplace_kernel<RB, TSA_F32><<<grid, 256, 0, s>>>(
-                                (const char*)oh, idx, (char*)out, d.H, d.L, d.keep));
+                                (const char*)oh, idx, (char*)out, d.H, heads_per_subset(d), d.L, d.keep));
   }
   return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-// Top-K token selection per (batch, query head): the subset S_h, ascending.
+// Top-K token selection per (batch, subset row): the subset S, ascending.
 //
 // The skill page "Token Sparse Attention Long Context", Step 1, keeps the top-scoring
 // tokens of each head; the paper page "Token Sparse Attention: Efficient Long-Context
@@ -8,7 +8,7 @@
 // the highest scores with ties to the lower position, and S_h is written in ascending
 // position order.
 //
-// One 1024-thread workgroup per (b, h) row.  Scores are >= 0, so their fp32 bit
+// One 1024-thread workgroup per (b, subset) row.  Scores are >= 0, so their fp32 bit
 // patterns order like the values.  The threshold T (the score of the last candidate
 // taken) is found by a three-pass radix select (11 + 11 + 10 bits) with LDS
 // histograms; then every wave compacts a contiguous segment of the row with wave
@@ -39,6 +39,20 @@ __device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* wave_tot) {
   for (int w = 0; w < wave; ++w) before += wave_tot[w];
   __syncthreads();
   return x + before;
+}
+
+// Per-KV-head subsets: the score row of KV head g is the fp32 sum, in ascending head
+// order, of the score rows of its G query heads (rows (b*R + g)*G + h' of [B][H][L]).
+__global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict__ scores, float* __restrict__ out,
+                                                        int G, int L, int64_t n) {
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t row = e / L;
+    const int64_t j = e - row * L;
+    const float* src = scores + row * G * L + j;
+    float acc = src[0];
+    for (int h = 1; h < G; ++h) acc += src[(int64_t)h * L];
+    out[e] = acc;
+  }
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __restrict__ scores,
@@ -168,11 +182,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, hipStream_t s) {
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, float* gsum,
+                         hipStream_t s) {
   const int Wp = d.W < d.L ? d.W : d.L;
   const int c1 = d.L - Wp;
   const int c0 = d.n_sink < c1 ? d.n_sink : c1;
-  select_kernel<<<d.B * d.H, SEL_THREADS, 0, s>>>(scores, idx, inv, d.L, d.keep, c0, c1);
+  const int R = subset_rows(d), G = heads_per_subset(d);
+  const float* rows = scores;
+  if (G > 1) {
+    const int64_t n = (int64_t)d.B * R * d.L;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+    group_sum_kernel<<<blocks, 256, 0, s>>>(scores, gsum, G, d.L, n);
+    rows = gsum;
+  }
+  select_kernel<<<d.B * R, SEL_THREADS, 0, s>>>(rows, idx, inv, d.L, d.keep, c0, c1);
   return hipGetLastError();
 }
 
