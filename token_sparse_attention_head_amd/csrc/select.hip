@@ -23,6 +23,7 @@ namespace {
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / TSA_WAVE;
 constexpr int SEL_MAX_BINS = 2048;
+constexpr int SEL_UNROLL = 8;      // loads in flight per thread in the streaming passes
 
 // Inclusive scan of one value per thread over the whole workgroup.
 __device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* wave_tot) {
@@ -84,9 +85,19 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
       const int nb = pass == 2 ? 1024 : 2048;
       for (int i = tid; i < nb; i += SEL_THREADS) hist[i] = 0;
       __syncthreads();
-      for (int j = c0 + tid; j < c1; j += SEL_THREADS) {
-        const uint32_t u = key[j];
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+      // SEL_UNROLL loads in flight per thread before any of them is used.
+      for (int j0 = c0 + tid; j0 < c1; j0 += SEL_UNROLL * SEL_THREADS) {
+        uint32_t u[SEL_UNROLL];
+#pragma unroll
+        for (int k = 0; k < SEL_UNROLL; ++k) {
+          const int j = j0 + k * SEL_THREADS;
+          u[k] = j < c1 ? key[j] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < SEL_UNROLL; ++k) {
+          const int j = j0 + k * SEL_THREADS;
+          if (j < c1 && (u[k] & pmask) == prefix) atomicAdd(&hist[(u[k] >> shift) & (nb - 1)], 1u);
+        }
       }
       __syncthreads();
       // Bins in descending order; thread t owns ranks [t*per, (t+1)*per).
@@ -124,21 +135,26 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
   const int beg = wave * seg;
   const int end = min(L, beg + seg);
 
-  auto classify = [&](int j, bool& strict, bool& eq) {
+  auto load_key = [&](int j) -> uint32_t { return (j < end && j >= c0 && j < c1) ? key[j] : 0u; };
+  auto classify = [&](int j, uint32_t u, bool& strict, bool& eq) {
     const bool valid = j < end;
     const bool cand = valid && j >= c0 && j < c1;
-    uint32_t u = 0;
-    if (cand) u = key[j];
     strict = (valid && !cand) || (cand && (take_all || (!take_none && u > T)));
     eq = cand && !take_all && !take_none && u == T;
   };
 
   uint32_t n_strict = 0, n_eq = 0;
-  for (int base = beg; base < end; base += TSA_WAVE) {
-    bool s, e;
-    classify(base + lane, s, e);
-    n_strict += __popcll(__ballot(s));
-    n_eq += __popcll(__ballot(e));
+  for (int base = beg; base < end; base += SEL_UNROLL * TSA_WAVE) {
+    uint32_t u[SEL_UNROLL];
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) u[k] = load_key(base + k * TSA_WAVE + lane);
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      bool s, e;
+      classify(base + k * TSA_WAVE + lane, u[k], s, e);
+      n_strict += __popcll(__ballot(s));
+      n_eq += __popcll(__ballot(e));
+    }
   }
   if (lane == 0) {
     seg_strict[wave] = n_strict;
@@ -162,21 +178,27 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
   int32_t* row_inv = inv ? inv + (int64_t)bh * L : nullptr;
   uint32_t pos = seg_out[wave];
   uint32_t eq_rank = seg_eq_before[wave];
-  for (int base = beg; base < end; base += TSA_WAVE) {
-    const int j = base + lane;
-    bool s, e;
-    classify(j, s, e);
-    const uint64_t emask = __ballot(e);
-    const uint32_t my_eq = eq_rank + __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0u));
-    const bool take = s || (e && my_eq < need_eq);
-    const uint64_t tmask = __ballot(take);
-    const uint32_t my_pos = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(tmask >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)tmask, 0u));
-    if (take && my_pos < (uint32_t)keep) row_idx[my_pos] = j;
-    if (row_inv && j < end) row_inv[j] = (take && my_pos < (uint32_t)keep) ? (int32_t)my_pos : -1;
-    pos += __popcll(tmask);
-    eq_rank += __popcll(emask);
+  for (int base = beg; base < end; base += SEL_UNROLL * TSA_WAVE) {
+    uint32_t u[SEL_UNROLL];
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) u[k] = load_key(base + k * TSA_WAVE + lane);
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int j = base + k * TSA_WAVE + lane;
+      bool s, e;
+      classify(j, u[k], s, e);
+      const uint64_t emask = __ballot(e);
+      const uint32_t my_eq = eq_rank + __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0u));
+      const bool take = s || (e && my_eq < need_eq);
+      const uint64_t tmask = __ballot(take);
+      const uint32_t my_pos = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(tmask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)tmask, 0u));
+      if (take && my_pos < (uint32_t)keep) row_idx[my_pos] = j;
+      if (row_inv && j < end) row_inv[j] = (take && my_pos < (uint32_t)keep) ? (int32_t)my_pos : -1;
+      pos += __popcll(tmask);
+      eq_rank += __popcll(emask);
+    }
   }
 }
 
