@@ -15,7 +15,8 @@ EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_check", "tsa_dense_attn", "tsa_f
 
 
 def D(**kw):
-    base = dict(B=1, H=32, Hkv=8, L=8192, d=128, keep=4096, W=64, n_sink=4, dtype=tsa.TSA_BF16, scale=0.0)
+    base = dict(B=1, H=32, Hkv=8, L=8192, d=128, keep=4096, W=64, n_sink=4, dtype=tsa.TSA_BF16, scale=0.0,
+                subsets=tsa.TSA_SUBSETS_PER_HEAD)
     base.update(kw)
     return tsa.make_desc(**base)
 
@@ -44,6 +45,8 @@ def test_header_declares_and_library_exports_every_entry_point():
     (dict(L=0, keep=0), 0),                    # empty problem: nothing to do
     (dict(B=0), 0),
     (dict(B=4096, H=32), 2),                   # grid limit
+    (dict(subsets=1), 0),                      # one subset per KV head
+    (dict(subsets=2), 9), (dict(subsets=-1), 9),
 ])
 def test_check_codes(kw, code):
     assert tsa.tsa_check(D(**kw)) == code
@@ -65,6 +68,13 @@ def test_workspace_sizes():
     assert e.value.status == 9
     with pytest.raises(tsa.TsaError):
         tsa.tsa_workspace_size(D(keep=3), tsa.TSA_OP_FORWARD)
+    # one subset per KV head: the select sums the 4 score rows of each group into [B, Hkv, L],
+    # the inverse map has Hkv rows, and the staged fp32 forward holds K^/V^ per KV head only
+    kv = D(subsets=tsa.TSA_SUBSETS_PER_KV_HEAD)
+    assert tsa.tsa_workspace_size(kv, tsa.TSA_OP_SELECT) == 8 * 8192 * 4
+    assert tsa.tsa_workspace_size(kv, tsa.TSA_OP_SCATTER) == 8 * 8192 * 4
+    kv32 = tsa.tsa_workspace_size(D(dtype=tsa.TSA_F32, subsets=1), tsa.TSA_OP_FORWARD)
+    assert 2 * 32 * 4096 * 128 * 4 + 2 * 8 * 4096 * 128 * 4 <= kv32 < fwd32
 
 
 A = 1 << 40           # fake, well-separated, 16-byte aligned addresses
@@ -109,6 +119,11 @@ def test_entry_points_reject_before_launch():
     assert call("tsa_forward", bd, q, k, v, r, o, None, None, k, big, None) == 7
     assert call("tsa_dense_attn", bd, q, k, v, v, None) == 7
     assert call("tsa_score", bd, q, k, q, ws, big, None) == 7
+    # one subset per KV head: the select needs its workspace of summed score rows
+    kvd = ctypes.byref(D(subsets=tsa.TSA_SUBSETS_PER_KV_HEAD))
+    assert call("tsa_select", kvd, sc, idx, None, 0, None) == 6
+    assert call("tsa_select", kvd, sc, idx, ws, 16, None) == 6
+    assert call("tsa_select", kvd, sc, idx, sc + 4096, big, None) == 7
     # descriptor errors come first
     bad = ctypes.byref(D(keep=2))
     assert call("tsa_forward", bad, q, k, v, r, o, None, None, ws, big, None) == 3
