@@ -194,13 +194,14 @@ def stage_only(tsa, torch, timer, w, x, name, reps):
     ws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
     sws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCORE)), dtype=torch.uint8, device="cuda")
     cws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_SCATTER)), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_SELECT), dtype=torch.uint8, device="cuda")
     tsa.tsa_forward(desc, q, k, v, r, out, scores, idx, ws)
     comp = [torch.empty(B, H, w.keep, D, dtype=dt, device="cuda") for _ in range(4)]
     tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2])
     o = torch.empty_like(q) if name == "dense" else None
     fns = {
         "score": lambda: tsa.tsa_score(desc, q, k, scores, sws),
-        "select": lambda: tsa.tsa_select(desc, scores, idx),
+        "select": lambda: tsa.tsa_select(desc, scores, idx, lws, lws.numel()),
         "gather": lambda: tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2]),
         "attn": lambda: tsa.tsa_attn(desc, comp[0], comp[1], comp[2], comp[3]),
         "scatter": lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r, out, cws),

@@ -116,8 +116,9 @@ tsa_status tsa_score(const tsa_desc* desc, const void* q, const void* k, float* 
  * position; written ascending to idx[b][r][0..keep).  The subset score is the head's
  * score row (per head) or, per KV head, the fp32 sum of the G rows of its query heads
  * taken in ascending head order.  Scores must be >= 0 (as tsa_score produces).  In:
- * scores [B][H][L].  Out: idx [B][R][keep].  Workspace: TSA_OP_SELECT (0 bytes per head,
- * ws may then be NULL; B*Hkv*L*4 bytes of summed scores per KV head). */
+ * scores [B][H][L].  Out: idx [B][R][keep].  Workspace: TSA_OP_SELECT (never 0: the
+ * radix-select histograms and counts, about 8 KiB per (b, r) row, plus B*Hkv*L*4 bytes of
+ * summed scores per KV head); its contents need no initialisation and are not kept. */
 tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx,
                       void* ws, size_t ws_bytes, void* stream);
 

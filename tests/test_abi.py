@@ -54,7 +54,8 @@ def test_check_codes(kw, code):
 
 def test_workspace_sizes():
     d = D()
-    assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) == 0
+    # the select's radix histograms (2048 bins) and per-wave counts for each of the 32 rows
+    assert 32 * 2048 * 4 <= tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) < 32 * 8192 * 4
     assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SCATTER) == 32 * 8192 * 4
     fwd = tsa.tsa_workspace_size(d, tsa.TSA_OP_FORWARD)
     # bf16 forward is fused: scores, idx and the inverse map, no compact tensors
@@ -71,7 +72,7 @@ def test_workspace_sizes():
     # one subset per KV head: the select sums the 4 score rows of each group into [B, Hkv, L],
     # the inverse map has Hkv rows, and the staged fp32 forward holds K^/V^ per KV head only
     kv = D(subsets=tsa.TSA_SUBSETS_PER_KV_HEAD)
-    assert tsa.tsa_workspace_size(kv, tsa.TSA_OP_SELECT) == 8 * 8192 * 4
+    assert 8 * 8192 * 4 + 8 * 2048 * 4 <= tsa.tsa_workspace_size(kv, tsa.TSA_OP_SELECT) < 2 * 8 * 8192 * 4
     assert tsa.tsa_workspace_size(kv, tsa.TSA_OP_SCATTER) == 8 * 8192 * 4
     kv32 = tsa.tsa_workspace_size(D(dtype=tsa.TSA_F32, subsets=1), tsa.TSA_OP_FORWARD)
     assert 2 * 32 * 4096 * 128 * 4 + 2 * 8 * 4096 * 128 * 4 <= kv32 < fwd32
@@ -119,10 +120,13 @@ def test_entry_points_reject_before_launch():
     assert call("tsa_forward", bd, q, k, v, r, o, None, None, k, big, None) == 7
     assert call("tsa_dense_attn", bd, q, k, v, v, None) == 7
     assert call("tsa_score", bd, q, k, q, ws, big, None) == 7
-    # one subset per KV head: the select needs its workspace of summed score rows
+    # the select always needs its workspace (per KV head it also holds the summed score rows)
+    assert call("tsa_select", bd, sc, idx, None, 0, None) == 6
+    assert call("tsa_select", bd, sc, idx, ws, 16, None) == 6
+    assert call("tsa_select", bd, sc, idx, idx + 64, big, None) == 7
     kvd = ctypes.byref(D(subsets=tsa.TSA_SUBSETS_PER_KV_HEAD))
     assert call("tsa_select", kvd, sc, idx, None, 0, None) == 6
-    assert call("tsa_select", kvd, sc, idx, ws, 16, None) == 6
+    assert call("tsa_select", kvd, sc, idx, ws, 8 * 8192 * 4, None) == 6
     assert call("tsa_select", kvd, sc, idx, sc + 4096, big, None) == 7
     # descriptor errors come first
     bad = ctypes.byref(D(keep=2))

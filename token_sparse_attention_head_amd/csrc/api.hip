@@ -94,9 +94,9 @@ tsa_status after_launch(hipError_t e, hipStream_t s) {
   } while (0)
 
 // Byte sizes of the tensors of a descriptor (idx, inv and the compact K/V have one row
-// per subset: H of them per head, Hkv per KV head; gsum holds the summed score rows).
+// per subset: H of them per head, Hkv per KV head; sel is the workspace of the select).
 struct Sizes {
-  size_t q, kv, scores, idx, compact, kvc, inv, gsum, part, stat;
+  size_t q, kv, scores, idx, compact, kvc, inv, sel, part, stat;
 };
 
 Sizes sizes_of(const tsa_desc& d) {
@@ -110,7 +110,7 @@ Sizes sizes_of(const tsa_desc& d) {
   z.compact = (size_t)d.B * d.H * d.keep * d.d * e;
   z.kvc = (size_t)d.B * R * d.keep * d.d * e;
   z.inv = (size_t)d.B * R * d.L * 4;
-  z.gsum = R < d.H ? (size_t)d.B * R * d.L * 4 : 0;
+  z.sel = tsa::select_layout(d).total;
   int chunk = 32, nchunk = 1;
   if (d.L > 0) tsa::score_chunking(d, chunk, nchunk);
   z.part = (size_t)d.B * d.H * nchunk * window(d) * 8;
@@ -122,7 +122,7 @@ Sizes sizes_of(const tsa_desc& d) {
 // bf16 forward is fused (attention reads the rows through idx and writes residual + O), so
 // it needs no compact tensors; the fp32 forward runs the stages one after the other.
 struct FwdLayout {
-  size_t scores, idx, inv, gsum, part, stat, qh, kh, vh, oh, total;
+  size_t scores, idx, inv, sel, part, stat, qh, kh, vh, oh, total;
 };
 
 FwdLayout fwd_layout(const tsa_desc& d) {
@@ -134,7 +134,7 @@ FwdLayout fwd_layout(const tsa_desc& d) {
   f.scores = o; o += round_up(z.scores);
   f.idx = o; o += round_up(z.idx);
   f.inv = o; o += round_up(z.inv);
-  f.gsum = o; o += round_up(z.gsum);
+  f.sel = o; o += round_up(z.sel);
   f.part = o; o += round_up(z.part);
   f.stat = o; o += round_up(z.stat);
   f.qh = o; o += comp;
@@ -180,7 +180,7 @@ tsa_status tsa_workspace_size(const tsa_desc* desc, int op, size_t* bytes) {
   const Sizes z = sizes_of(*desc);
   switch (op) {
     case TSA_OP_SCORE: *bytes = round_up(z.part) + round_up(z.stat); break;
-    case TSA_OP_SELECT: *bytes = round_up(z.gsum); break;
+    case TSA_OP_SELECT: *bytes = round_up(z.sel); break;
     case TSA_OP_SCATTER: *bytes = round_up(z.inv); break;
     case TSA_OP_FORWARD: *bytes = fwd_layout(*desc).total; break;
     default: return TSA_ERR_ARG;
@@ -216,13 +216,11 @@ tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx, v
   if (!aligned(scores) || !aligned(idx) || !aligned(ws)) return TSA_ERR_ALIGN;
   const Sizes z = sizes_of(d);
   if (overlap({scores, z.scores}, {idx, z.idx})) return TSA_ERR_ALIAS;
-  const size_t need = round_up(z.gsum);
-  if (need > 0) {
-    if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
-    if (overlap({ws, need}, {scores, z.scores}) || overlap({ws, need}, {idx, z.idx})) return TSA_ERR_ALIAS;
-  }
+  const size_t need = round_up(z.sel);
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (overlap({ws, need}, {scores, z.scores}) || overlap({ws, need}, {idx, z.idx})) return TSA_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(tsa::launch_select(d, scores, idx, nullptr, static_cast<float*>(ws), s), s);
+  return after_launch(tsa::launch_select(d, scores, idx, nullptr, ws, s), s);
 }
 
 tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -314,7 +312,7 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   void* oh = at<char>(ws, f.oh);
   const bool in_place = out == residual;
   TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
-  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, at<float>(ws, f.gsum), s), s));
+  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, at<char>(ws, f.sel), s), s));
   if (fused_forward(d)) {
     // Rows a head does not keep are the residual (copied out of place, untouched in place);
     // the attention epilogue writes residual + O into the kept rows.

@@ -17,8 +17,16 @@ void score_chunking(const tsa_desc& d, int& chunk, int& nchunk);
 
 hipError_t launch_score(const tsa_desc& d, const void* q, const void* k, float* scores, float2* part, float2* stat,
                         hipStream_t s);
-// Per-KV-head subsets sum the score rows of each group into gsum ([B][Hkv][L], workspace).
-hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, float* gsum,
+// Workspace of the select (each region 256-byte aligned): the summed score rows of a
+// KV group (subsets per KV head only), the per-row state of the radix select, the
+// per-row global histograms and the per-wave counts of the compaction.  S position
+// slices of seg positions per row.
+struct SelectLayout {
+  size_t gsum, state, hist, counts, total;
+  int S, seg;
+};
+SelectLayout select_layout(const tsa_desc& d);
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, void* ws,
                          hipStream_t s);
 hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              void* qh, void* kh, void* vh, hipStream_t s);

@@ -8,11 +8,11 @@
 // the highest scores with ties to the lower position, and S_h is written in ascending
 // position order.
 //
-// One 1024-thread workgroup per (b, subset) row.  Scores are >= 0, so their fp32 bit
-// patterns order like the values.  The threshold T (the score of the last candidate
-// taken) is found by a three-pass radix select (11 + 11 + 10 bits) with LDS
-// histograms; then every wave compacts a contiguous segment of the row with wave
-// ballots and mbcnt prefix counts, ties at T going to the lowest positions.
+// Scores are >= 0, so their fp32 bit patterns order like the values.  The threshold T
+// (the score of the last candidate taken) is found by a three-pass radix select
+// (11 + 11 + 10 bits) whose histograms are built by many workgroups per row; then every
+// wave compacts its own contiguous range of positions with wave ballots and mbcnt prefix
+// counts, ties at T going to the lowest positions.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,6 +24,7 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / TSA_WAVE;
 constexpr int SEL_MAX_BINS = 2048;
 constexpr int SEL_UNROLL = 8;      // loads in flight per thread in the streaming passes
+constexpr int SEL_MAX_SLICES = 64; // position slices (workgroups) per row
 
 // Inclusive scan of one value per thread over the whole workgroup.
 __device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* wave_tot) {
@@ -56,146 +57,225 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict_
   }
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __restrict__ scores,
-                                                             int32_t* __restrict__ idx, int32_t* __restrict__ inv,
-                                                             int L, int keep, int c0, int c1) {
-  // Candidates are the positions [c0, c1); [0, c0) and [c1, L) are forced.
-  __shared__ uint32_t hist[SEL_MAX_BINS];
-  __shared__ uint32_t wave_tot[SEL_WAVES];
-  __shared__ uint32_t found_bin, found_above;
-  __shared__ uint32_t seg_strict[SEL_WAVES], seg_eq[SEL_WAVES];
-  __shared__ uint32_t seg_out[SEL_WAVES], seg_eq_before[SEL_WAVES];
+// ---- multi-workgroup radix select --------------------------------------------------
+//
+// A row is split into S position slices of seg positions (seg a multiple of 256), one
+// 256-thread workgroup each, so every CU helps even when there are few rows.  Per-row
+// state in the workspace: need (candidates still to take), prefix and pmask of the
+// threshold key found so far, and mode (0: threshold needed, 1: take every candidate,
+// 2: take none).  Each pass: every slice builds an LDS histogram of the candidates that
+// match the prefix and adds it to the row's global histogram; one workgroup per row then
+// scans it from the top, narrows the prefix and clears the histogram.  After three
+// passes the prefix is the threshold key T and need is the number of candidates equal
+// to T to take (lowest positions first).  Compaction: every wave of every slice counts
+// its strict and equal positions; then every wave writes its positions at the offset the
+// counts of all earlier waves give, in position order.
+constexpr int SEL_WG = 256;
+constexpr int SEL_WG_WAVES = SEL_WG / TSA_WAVE;
 
-  const int bh = blockIdx.x;
-  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)bh * L);
-  const int tid = threadIdx.x;
-  const int n_cand = c1 - c0;
-  const int n_forced = L - n_cand;
-  uint32_t need = (uint32_t)(keep - n_forced);   // candidates still to take
-  const bool take_all = (int)need >= n_cand;
-  const bool take_none = need == 0;
+struct SelGeom {
+  int L, keep, c0, c1, S, seg;
+};
 
-  uint32_t T = 0xFFFFFFFFu;   // threshold key
-  uint32_t need_eq = 0;       // how many candidates equal to T are taken (lowest positions first)
-  if (!take_all && !take_none) {
-    uint32_t prefix = 0, pmask = 0;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nb = pass == 2 ? 1024 : 2048;
-      for (int i = tid; i < nb; i += SEL_THREADS) hist[i] = 0;
-      __syncthreads();
-      // SEL_UNROLL loads in flight per thread before any of them is used.
-      for (int j0 = c0 + tid; j0 < c1; j0 += SEL_UNROLL * SEL_THREADS) {
-        uint32_t u[SEL_UNROLL];
-#pragma unroll
-        for (int k = 0; k < SEL_UNROLL; ++k) {
-          const int j = j0 + k * SEL_THREADS;
-          u[k] = j < c1 ? key[j] : 0u;
-        }
-#pragma unroll
-        for (int k = 0; k < SEL_UNROLL; ++k) {
-          const int j = j0 + k * SEL_THREADS;
-          if (j < c1 && (u[k] & pmask) == prefix) atomicAdd(&hist[(u[k] >> shift) & (nb - 1)], 1u);
-        }
-      }
-      __syncthreads();
-      // Bins in descending order; thread t owns ranks [t*per, (t+1)*per).
-      const int per = nb / SEL_THREADS;
-      uint32_t local = 0;
-      for (int q = 0; q < per; ++q) local += hist[nb - 1 - (tid * per + q)];
-      const uint32_t incl = block_inclusive_scan(local, wave_tot);
-      const uint32_t excl = incl - local;
-      if (excl < need && need <= incl) {
-        uint32_t cum = excl;
-        for (int q = 0; q < per; ++q) {
-          const int bin = nb - 1 - (tid * per + q);
-          if (cum + hist[bin] >= need) {
-            found_bin = bin;
-            found_above = cum;
-            break;
-          }
-          cum += hist[bin];
-        }
-      }
-      __syncthreads();
-      need -= found_above;
-      prefix |= found_bin << shift;
-      pmask |= (uint32_t)(nb - 1) << shift;
-      __syncthreads();
-    }
-    T = prefix;
-    need_eq = need;
+__device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ int sel_bins(int pass) { return pass == 2 ? 1024 : SEL_MAX_BINS; }
+
+__global__ __launch_bounds__(SEL_WG) void sel_init_kernel(uint32_t* __restrict__ state, uint32_t* __restrict__ hist,
+                                                          SelGeom g) {
+  const int row = blockIdx.x;
+  for (int i = threadIdx.x; i < SEL_MAX_BINS; i += SEL_WG) hist[(int64_t)row * SEL_MAX_BINS + i] = 0;
+  if (threadIdx.x == 0) {
+    const int n_cand = g.c1 - g.c0;
+    const int need = g.keep - (g.L - n_cand);
+    uint32_t* st = state + (int64_t)row * 4;
+    st[0] = (uint32_t)need;
+    st[1] = 0;
+    st[2] = 0;
+    st[3] = need >= n_cand ? 1u : (need == 0 ? 2u : 0u);
   }
+}
 
-  // Compaction: wave w owns positions [w*seg, (w+1)*seg).
-  const int lane = lane_id();
-  const int wave = tid / TSA_WAVE;
-  const int seg = ((L + SEL_WAVES - 1) / SEL_WAVES + TSA_WAVE - 1) / TSA_WAVE * TSA_WAVE;
-  const int beg = wave * seg;
-  const int end = min(L, beg + seg);
+__global__ __launch_bounds__(SEL_WG) void sel_hist_kernel(const float* __restrict__ scores,
+                                                          const uint32_t* __restrict__ state,
+                                                          uint32_t* __restrict__ hist, SelGeom g, int pass) {
+  __shared__ uint32_t lh[SEL_MAX_BINS];
+  const int row = blockIdx.y;
+  const uint32_t* st = state + (int64_t)row * 4;
+  if (st[3] != 0) return;
+  const uint32_t prefix = st[1], pmask = st[2];
+  const int shift = sel_shift(pass), nb = sel_bins(pass);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nb; i += SEL_WG) lh[i] = 0;
+  __syncthreads();
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)row * g.L);
+  const int beg = max(g.c0, blockIdx.x * g.seg);
+  const int end = min(g.c1, (blockIdx.x + 1) * g.seg);
+  for (int j0 = beg + tid; j0 < end; j0 += SEL_UNROLL * SEL_WG) {
+    uint32_t u[SEL_UNROLL];
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int j = j0 + k * SEL_WG;
+      u[k] = j < end ? key[j] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int j = j0 + k * SEL_WG;
+      if (j < end && (u[k] & pmask) == prefix) atomicAdd(&lh[(u[k] >> shift) & (nb - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (int64_t)row * SEL_MAX_BINS;
+  for (int i = tid; i < nb; i += SEL_WG)
+    if (lh[i] != 0) atomicAdd(&gh[i], lh[i]);
+}
 
-  auto load_key = [&](int j) -> uint32_t { return (j < end && j >= c0 && j < c1) ? key[j] : 0u; };
-  auto classify = [&](int j, uint32_t u, bool& strict, bool& eq) {
-    const bool valid = j < end;
+__global__ __launch_bounds__(SEL_THREADS) void sel_find_kernel(uint32_t* __restrict__ state, uint32_t* __restrict__ hist,
+                                                               int pass) {
+  __shared__ uint32_t wave_tot[SEL_WAVES];
+  const int row = blockIdx.x;
+  uint32_t* st = state + (int64_t)row * 4;
+  if (st[3] != 0) return;
+  const uint32_t need = st[0];
+  const int shift = sel_shift(pass), nb = sel_bins(pass);
+  const int tid = threadIdx.x;
+  uint32_t* gh = hist + (int64_t)row * SEL_MAX_BINS;
+  // Bins in descending order; thread t owns ranks [t*per, (t+1)*per).
+  const int per = nb / SEL_THREADS;
+  uint32_t cnt[SEL_MAX_BINS / SEL_THREADS];
+  uint32_t local = 0;
+  for (int q = 0; q < per; ++q) {
+    cnt[q] = gh[nb - 1 - (tid * per + q)];
+    local += cnt[q];
+  }
+  const uint32_t incl = block_inclusive_scan(local, wave_tot);
+  const uint32_t excl = incl - local;
+  if (excl < need && need <= incl) {
+    uint32_t cum = excl;
+    for (int q = 0; q < per; ++q) {
+      if (cum + cnt[q] >= need) {
+        const uint32_t bin = (uint32_t)(nb - 1 - (tid * per + q));
+        st[0] = need - cum;
+        st[1] |= bin << shift;
+        st[2] |= (uint32_t)(nb - 1) << shift;
+        break;
+      }
+      cum += cnt[q];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += SEL_THREADS) gh[i] = 0;   // clear for the next pass
+}
+
+// Whether position j (of a wave's range) is a forced or above-threshold position (strict)
+// or a candidate equal to the threshold (eq).
+struct SelRule {
+  int c0, c1;
+  uint32_t T;
+  bool take_all, take_none;
+  __device__ __forceinline__ void classify(int j, bool valid, uint32_t u, bool& strict, bool& eq) const {
     const bool cand = valid && j >= c0 && j < c1;
     strict = (valid && !cand) || (cand && (take_all || (!take_none && u > T)));
     eq = cand && !take_all && !take_none && u == T;
-  };
+  }
+};
 
+__device__ __forceinline__ SelRule sel_rule(const uint32_t* st, const SelGeom& g) {
+  SelRule r;
+  r.c0 = g.c0;
+  r.c1 = g.c1;
+  r.take_all = st[3] == 1;
+  r.take_none = st[3] == 2;
+  r.T = st[1];
+  return r;
+}
+
+__global__ __launch_bounds__(SEL_WG) void sel_count_kernel(const float* __restrict__ scores,
+                                                           const uint32_t* __restrict__ state,
+                                                           uint32_t* __restrict__ counts, SelGeom g) {
+  const int row = blockIdx.y, s = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
+  const SelRule rule = sel_rule(state + (int64_t)row * 4, g);
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)row * g.L);
+  const int wseg = g.seg / SEL_WG_WAVES;
+  const int beg = s * g.seg + wave * wseg;
+  const int end = min(g.L, beg + wseg);
   uint32_t n_strict = 0, n_eq = 0;
   for (int base = beg; base < end; base += SEL_UNROLL * TSA_WAVE) {
     uint32_t u[SEL_UNROLL];
 #pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) u[k] = load_key(base + k * TSA_WAVE + lane);
-#pragma unroll
     for (int k = 0; k < SEL_UNROLL; ++k) {
-      bool s, e;
-      classify(base + k * TSA_WAVE + lane, u[k], s, e);
-      n_strict += __popcll(__ballot(s));
-      n_eq += __popcll(__ballot(e));
+      const int j = base + k * TSA_WAVE + lane;
+      u[k] = (j < end && j >= rule.c0 && j < rule.c1) ? key[j] : 0u;
     }
-  }
-  if (lane == 0) {
-    seg_strict[wave] = n_strict;
-    seg_eq[wave] = n_eq;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t eq_before = 0, out = 0;
-    for (int w = 0; w < SEL_WAVES; ++w) {
-      const uint32_t rem = need_eq > eq_before ? need_eq - eq_before : 0;
-      const uint32_t take_eq = min(rem, seg_eq[w]);
-      seg_eq_before[w] = eq_before;
-      seg_out[w] = out;
-      out += seg_strict[w] + take_eq;
-      eq_before += seg_eq[w];
-    }
-  }
-  __syncthreads();
-
-  int32_t* row_idx = idx + (int64_t)bh * keep;
-  int32_t* row_inv = inv ? inv + (int64_t)bh * L : nullptr;
-  uint32_t pos = seg_out[wave];
-  uint32_t eq_rank = seg_eq_before[wave];
-  for (int base = beg; base < end; base += SEL_UNROLL * TSA_WAVE) {
-    uint32_t u[SEL_UNROLL];
-#pragma unroll
-    for (int k = 0; k < SEL_UNROLL; ++k) u[k] = load_key(base + k * TSA_WAVE + lane);
 #pragma unroll
     for (int k = 0; k < SEL_UNROLL; ++k) {
       const int j = base + k * TSA_WAVE + lane;
-      bool s, e;
-      classify(j, u[k], s, e);
+      bool st, eq;
+      rule.classify(j, j < end, u[k], st, eq);
+      n_strict += __popcll(__ballot(st));
+      n_eq += __popcll(__ballot(eq));
+    }
+  }
+  if (lane == 0) {
+    uint32_t* c = counts + (((int64_t)row * g.S + s) * SEL_WG_WAVES + wave) * 2;
+    c[0] = n_strict;
+    c[1] = n_eq;
+  }
+}
+
+__global__ __launch_bounds__(SEL_WG) void sel_write_kernel(const float* __restrict__ scores,
+                                                           const uint32_t* __restrict__ state,
+                                                           const uint32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ idx, int32_t* __restrict__ inv,
+                                                           SelGeom g) {
+  const int row = blockIdx.y, s = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
+  const uint32_t* st = state + (int64_t)row * 4;
+  const SelRule rule = sel_rule(st, g);
+  const uint32_t need_eq = (rule.take_all || rule.take_none) ? 0u : st[0];
+  // This wave's offset: the strict positions of every earlier wave of the row plus the
+  // equal ones they take, min(need_eq, equal positions before this wave).
+  const int my_w = s * SEL_WG_WAVES + wave;
+  const uint32_t* crow = counts + (int64_t)row * g.S * SEL_WG_WAVES * 2;
+  uint32_t n_st = 0, n_eq = 0;
+  for (int w = lane; w < my_w; w += TSA_WAVE) {
+    n_st += crow[2 * w];
+    n_eq += crow[2 * w + 1];
+  }
+#pragma unroll
+  for (int o = TSA_WAVE / 2; o > 0; o >>= 1) {
+    n_st += __shfl_xor(n_st, o, TSA_WAVE);
+    n_eq += __shfl_xor(n_eq, o, TSA_WAVE);
+  }
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)row * g.L);
+  int32_t* row_idx = idx + (int64_t)row * g.keep;
+  int32_t* row_inv = inv ? inv + (int64_t)row * g.L : nullptr;
+  const int wseg = g.seg / SEL_WG_WAVES;
+  const int beg = s * g.seg + wave * wseg;
+  const int end = min(g.L, beg + wseg);
+  uint32_t pos = n_st + min(need_eq, n_eq);
+  uint32_t eq_rank = n_eq;
+  for (int base = beg; base < end; base += SEL_UNROLL * TSA_WAVE) {
+    uint32_t u[SEL_UNROLL];
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int j = base + k * TSA_WAVE + lane;
+      u[k] = (j < end && j >= rule.c0 && j < rule.c1) ? key[j] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < SEL_UNROLL; ++k) {
+      const int j = base + k * TSA_WAVE + lane;
+      bool strict, e;
+      rule.classify(j, j < end, u[k], strict, e);
       const uint64_t emask = __ballot(e);
       const uint32_t my_eq = eq_rank + __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0u));
-      const bool take = s || (e && my_eq < need_eq);
+      const bool take = strict || (e && my_eq < need_eq);
       const uint64_t tmask = __ballot(take);
       const uint32_t my_pos = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(tmask >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)tmask, 0u));
-      if (take && my_pos < (uint32_t)keep) row_idx[my_pos] = j;
-      if (row_inv && j < end) row_inv[j] = (take && my_pos < (uint32_t)keep) ? (int32_t)my_pos : -1;
+      if (take && my_pos < (uint32_t)g.keep) row_idx[my_pos] = j;
+      if (row_inv && j < end) row_inv[j] = (take && my_pos < (uint32_t)g.keep) ? (int32_t)my_pos : -1;
       pos += __popcll(tmask);
       eq_rank += __popcll(emask);
     }
@@ -204,20 +284,52 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, float* gsum,
+SelectLayout select_layout(const tsa_desc& d) {
+  const int64_t rows = (int64_t)d.B * subset_rows(d);
+  SelectLayout y;
+  // About 512 workgroups per pass, at least 256 positions per slice.
+  int S = (int)std::min<int64_t>(std::max<int64_t>((512 + rows - 1) / std::max<int64_t>(rows, 1), 1), SEL_MAX_SLICES);
+  const int L = d.L > 0 ? d.L : 1;
+  y.seg = ((L + S - 1) / S + SEL_WG - 1) / SEL_WG * SEL_WG;
+  y.S = (L + y.seg - 1) / y.seg;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t o = 0;
+  y.gsum = o; o += heads_per_subset(d) > 1 ? up((size_t)rows * d.L * 4) : 0;
+  y.state = o; o += up((size_t)rows * 4 * 4);
+  y.hist = o; o += up((size_t)rows * SEL_MAX_BINS * 4);
+  y.counts = o; o += up((size_t)rows * y.S * SEL_WG_WAVES * 2 * 4);
+  y.total = o;
+  return y;
+}
+
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, void* ws,
                          hipStream_t s) {
   const int Wp = d.W < d.L ? d.W : d.L;
   const int c1 = d.L - Wp;
   const int c0 = d.n_sink < c1 ? d.n_sink : c1;
   const int R = subset_rows(d), G = heads_per_subset(d);
-  const float* rows = scores;
+  const int rows = d.B * R;
+  const SelectLayout y = select_layout(d);
+  char* base = static_cast<char*>(ws);
+  const float* src = scores;
   if (G > 1) {
-    const int64_t n = (int64_t)d.B * R * d.L;
+    float* gsum = reinterpret_cast<float*>(base + y.gsum);
+    const int64_t n = (int64_t)rows * d.L;
     const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
     group_sum_kernel<<<blocks, 256, 0, s>>>(scores, gsum, G, d.L, n);
-    rows = gsum;
+    src = gsum;
   }
-  select_kernel<<<d.B * R, SEL_THREADS, 0, s>>>(rows, idx, inv, d.L, d.keep, c0, c1);
+  uint32_t* state = reinterpret_cast<uint32_t*>(base + y.state);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + y.hist);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(base + y.counts);
+  const SelGeom g{d.L, d.keep, c0, c1, y.S, y.seg};
+  sel_init_kernel<<<rows, SEL_WG, 0, s>>>(state, hist, g);
+  for (int pass = 0; pass < 3; ++pass) {
+    sel_hist_kernel<<<dim3(y.S, rows), SEL_WG, 0, s>>>(src, state, hist, g, pass);
+    sel_find_kernel<<<rows, SEL_THREADS, 0, s>>>(state, hist, pass);
+  }
+  sel_count_kernel<<<dim3(y.S, rows), SEL_WG, 0, s>>>(src, state, counts, g);
+  sel_write_kernel<<<dim3(y.S, rows), SEL_WG, 0, s>>>(src, state, counts, idx, inv, g);
   return hipGetLastError();
 }
 
