@@ -34,6 +34,16 @@ sum of the G heads' score rows, taken in ascending head order in the scores' own
 Every other stage is unchanged except that head h uses S_{h // G} and the compact K/V
 rows are held once per subset.
 
+Adaptive budgets (``tau`` / ``coverage_budget``): the paper page's TL;DR says per-head
+sparsity budgets adapt on the fly through a dynamic token coverage, and its Figures 1 and
+5 call tau the token coverage, a sparsity level where a higher value is sparser (0.005 in
+Figure 5).  The pages give no formula, so the reading here is: a subset row drops its
+lowest-scoring non-forced positions, one at a time in the reverse of the keep order,
+while their scores add up to at most tau times the row's total score; the budget K_h is
+what remains, capped at ``keep``.  Scores are counted in whole units of 2^-40 (each score
+rounded down) so that the integer K_h is decided by exact integer sums.  Rows with
+K_h < keep are padded with -1 in idx; gather gives zero rows there and scatter skips them.
+
 Every function works in float64; bf16 and fp32 inputs widen to float64 exactly.
 The readings taken where the pages are silent (window, causality, ties, order, the
 residual everywhere, the GQA head map, scale 1/sqrt(head_dim)) are stated at each
@@ -41,11 +51,14 @@ function.  Non-finite inputs are rejected.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
     "window", "forced_positions", "score", "score_head", "select", "select_row",
     "gather", "attend", "attend_rows", "scatter_residual", "forward", "threshold", "group_scores",
+    "MASS_UNIT_BITS", "mass_units", "coverage_budget_row", "coverage_budget",
 ]
 
 
@@ -140,18 +153,72 @@ def group_scores(s, kv_heads: int) -> np.ndarray:
     return out
 
 
-def select(s, keep: int, W: int, n_sink: int, kv_heads: int | None = None) -> np.ndarray:
-    """idx [B,R,keep] (int64, strictly ascending per subset) from scores [B,H,L]: one
-    subset per query head (R = H), or with ``kv_heads`` one per KV head on
-    ``group_scores`` (R = kv_heads)."""
+MASS_UNIT_BITS = 40
+
+
+def mass_units(s_row) -> list:
+    """Each score as a whole number of 2^-40 units, rounded down (Python integers; exact,
+    since multiplying a float by 2^40 only moves its exponent)."""
+    return [int(math.floor(float(x) * 2.0 ** MASS_UNIT_BITS)) for x in np.asarray(s_row, dtype=np.float64)]
+
+
+def coverage_budget_row(s_row, keep: int, W: int, n_sink: int, tau: float) -> int:
+    """K_h of one subset row under token coverage tau (paper page: TL;DR, Figures 1 and 5;
+    the rule is this library's reading, stated in the module docstring).
+
+    Mass budget: floor(tau * total), with tau taken as a float32 value and the product
+    formed in float64, total = the sum of all L scores in units.  Positions leave in the
+    reverse of the keep order (lower score first, among equal scores the higher position
+    first) while the mass that left stays within the budget; forced positions never leave.
+    """
+    units = mass_units(s_row)
+    L = len(units)
+    F = forced_positions(L, W, n_sink)
+    if not (len(F) <= keep <= L):
+        raise ValueError(f"keep={keep} outside [{len(F)}, {L}]")
+    s_row = np.asarray(s_row, dtype=np.float64)
+    budget = int(math.floor(float(np.float32(tau)) * float(sum(units))))
+    is_forced = np.zeros(L, dtype=bool)
+    is_forced[F] = True
+    cand = np.nonzero(~is_forced)[0]
+    leave_order = cand[np.lexsort((-cand, s_row[cand]))]   # primary: score ascending; then position descending
+    spent, left = 0, 0
+    for j in leave_order:
+        if spent + units[j] > budget:
+            break
+        spent += units[j]
+        left += 1
+    return min(L - left, keep)
+
+
+def coverage_budget(s, keep: int, W: int, n_sink: int, tau: float, kv_heads: int | None = None) -> np.ndarray:
+    """K_h for every subset row: [B,H,L] scores -> [B,R] int64 (R = H, or ``kv_heads``
+    rows of ``group_scores``)."""
     if kv_heads is not None:
         s = group_scores(s, kv_heads)
-    s = np.asarray(s, dtype=np.float64)
-    B, R, _ = s.shape
-    idx = np.empty((B, R, keep), dtype=np.int64)
+    B, R, _ = np.asarray(s).shape
+    out = np.empty((B, R), dtype=np.int64)
     for b in range(B):
         for r in range(R):
-            idx[b, r] = select_row(s[b, r], keep, W, n_sink)
+            out[b, r] = coverage_budget_row(s[b, r], keep, W, n_sink, tau)
+    return out
+
+
+def select(s, keep: int, W: int, n_sink: int, kv_heads: int | None = None, tau: float | None = None) -> np.ndarray:
+    """idx [B,R,keep] (int64, strictly ascending per subset) from scores [B,H,L]: one
+    subset per query head (R = H), or with ``kv_heads`` one per KV head on
+    ``group_scores`` (R = kv_heads).  With ``tau`` > 0 row r holds its K_r =
+    ``coverage_budget`` positions, then -1 up to ``keep``."""
+    if kv_heads is not None:
+        s = group_scores(s, kv_heads)
+    B, R, _ = np.asarray(s).shape
+    counts = coverage_budget(s, keep, W, n_sink, tau) if tau else None
+    s = np.asarray(s, dtype=np.float64)
+    idx = np.full((B, R, keep), -1, dtype=np.int64)
+    for b in range(B):
+        for r in range(R):
+            kr = keep if counts is None else int(counts[b, r])
+            idx[b, r, :kr] = select_row(s[b, r], kr, W, n_sink)
     return idx
 
 
@@ -173,7 +240,8 @@ def gather(q, k, v, idx):
     """Q^[b,h,t] = Q[b,S_t,h]; K^[b,r,t] = K[b,S_t,g]; V^[b,r,t] = V[b,S_t,g], where
     query head h uses subset r = h // (H/R) and g = h // G is its KV head (skill page,
     Step 2, gather by index; Figure 3, stage 1).  idx [B,R,keep] -> Q^ [B,H,keep,d],
-    K^, V^ [B,R,keep,d] (R = H: per head, one copy of the K/V rows per query head)."""
+    K^, V^ [B,R,keep,d] (R = H: per head, one copy of the K/V rows per query head).
+    Padding entries (-1) give zero rows."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, L, H, d = q.shape
     G = H // k.shape[2]
@@ -182,13 +250,15 @@ def gather(q, k, v, idx):
     qh = np.empty((B, H, keep, d))
     kh = np.empty((B, R, keep, d))
     vh = np.empty((B, R, keep, d))
+    valid = (idx >= 0)[..., None]
+    safe = np.where(idx >= 0, idx, 0)
     for b in range(B):
         for h in range(H):
-            qh[b, h] = q[b, idx[b, h // SG], h, :]
+            qh[b, h] = np.where(valid[b, h // SG], q[b, safe[b, h // SG], h, :], 0.0)
         for r in range(R):
             g = (r * SG) // G
-            kh[b, r] = k[b, idx[b, r], g, :]
-            vh[b, r] = v[b, idx[b, r], g, :]
+            kh[b, r] = np.where(valid[b, r], k[b, safe[b, r], g, :], 0.0)
+            vh[b, r] = np.where(valid[b, r], v[b, safe[b, r], g, :], 0.0)
     return qh, kh, vh
 
 
@@ -232,24 +302,26 @@ def attend_rows(qh_bh, kh_bh, vh_bh, rows, scale: float) -> np.ndarray:
 def scatter_residual(oh, idx, r) -> np.ndarray:
     """Out[b,p,h] = R[b,p,h] + O^[b,h,rank(p)] if p is in S_h, else R[b,p,h] (the compact
     outputs scattered into a zero full-length tensor, then the residual added: Figure 3,
-    stage 2; skill page, Step 2)."""
+    stage 2; skill page, Step 2).  Padding entries (-1) of idx are skipped."""
     oh, r = _f64(oh), _f64(r)
     out = r.copy()
     B, H, n, _ = oh.shape
     SG = H // idx.shape[1]                    # query heads per subset
     for b in range(B):
         for h in range(H):
-            out[b, idx[b, h // SG], h, :] += oh[b, h]
+            row = idx[b, h // SG]
+            ok = row >= 0
+            out[b, row[ok], h, :] += oh[b, h][ok]
     return out
 
 
 def forward(q, k, v, r, keep: int, W: int, n_sink: int, scale: float | None = None,
-            per_kv_head: bool = False) -> dict:
+            per_kv_head: bool = False, tau: float | None = None) -> dict:
     """All five stages; returns scores, idx, the compact tensors, O^ and Out."""
     d = np.asarray(q).shape[-1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     s = score(q, k, W, scale)
-    idx = select(s, keep, W, n_sink, np.asarray(k).shape[2] if per_kv_head else None)
+    idx = select(s, keep, W, n_sink, np.asarray(k).shape[2] if per_kv_head else None, tau)
     qh, kh, vh = gather(q, k, v, idx)
     oh = attend(qh, kh, vh, scale)
     out = scatter_residual(oh, idx, r)

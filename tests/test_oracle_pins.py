@@ -335,3 +335,111 @@ def test_group_forward_equals_per_head_when_queries_coincide():
     b = oracle.forward(q, x["k"], x["v"], x["r"], 20, 6, 2)
     assert np.array_equal(a["idx"][:, [0, 0, 1, 1]], b["idx"])
     assert np.array_equal(a["out"], b["out"])
+
+
+# ---- adaptive budgets (token coverage tau) --------------------------------------------
+# The rule is this library's reading of the paper page's token coverage (TL;DR, Figures 1
+# and 5): lowest-scoring non-forced positions leave while their summed score stays within
+# tau times the row's total; masses are counted in 2^-40 units.
+
+def test_mass_units_exact():
+    assert oracle.mass_units([0.5, 2.0 ** -40, 2.0 ** -41, 3.0, 0.0]) == [2 ** 39, 1, 0, 3 * 2 ** 40, 0]
+    x = float(np.float32(0.1))                    # not dyadic-short: rounds down
+    assert oracle.mass_units([x])[0] == int(Fraction(x) * 2 ** 40)
+
+
+def test_coverage_hand_case():
+    # L=12, W=2, one sink: forced {0, 10, 11}.  Total 16.8125; tau=0.1 (float32 0.100000001..)
+    # gives a budget just above 1.68125.  Leaving order (score up, then position down):
+    # 6 (.0625) 8 (.125) 3 (.125) 4 (.25) 1 (.25) 9 (.5) 2 (.5) 5 (1) 7 (2); cumulative
+    # .0625 .1875 .3125 .5625 .8125 1.3125 | 1.8125 > budget, so six leave and 2 (tied with
+    # 9) stays: K = 6, S = {0, 2, 5, 7, 10, 11}.
+    s = np.array([[[5, 0.25, 0.5, 0.125, 0.25, 1, 0.0625, 2, 0.125, 0.5, 3, 4]]], dtype=np.float64)
+    assert oracle.coverage_budget(s, 12, 2, 1, 0.1).tolist() == [[6]]
+    assert oracle.select(s, 12, 2, 1, tau=0.1)[0, 0].tolist() == [0, 2, 5, 7, 10, 11] + [-1] * 6
+    # the cap: at most keep positions
+    assert oracle.select(s, 5, 2, 1, tau=0.1)[0, 0].tolist() == [0, 5, 7, 10, 11]
+    # six leave once the budget reaches 1.3125, five just below it
+    assert oracle.coverage_budget_row(s[0, 0], 12, 2, 1, 0.0781) == 6     # budget 1.31306
+    assert oracle.coverage_budget_row(s[0, 0], 12, 2, 1, 0.078) == 7      # budget 1.31138
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_coverage_brute_force_max_leavers(seed):
+    # The number of positions that leave is the largest number of non-forced positions
+    # whose unit masses fit in the budget (exhaustive over subsets), and the kept set is
+    # the top-K set of the fixed-budget rule.
+    rng = np.random.default_rng(seed)
+    L, W, ns = 10, 2, 1
+    s = np.round(rng.random(L) * 8) / 8 + rng.integers(0, 2, L) * rng.random(L)
+    units = oracle.mass_units(s)
+    F = set(oracle.forced_positions(L, W, ns).tolist())
+    cand = [j for j in range(L) if j not in F]
+    for tau in (0.0001, 0.02, 0.1, 0.3, 0.7, 1.0):
+        budget = math.floor(float(np.float32(tau)) * float(sum(units)))
+        best = 0
+        for mask in range(1 << len(cand)):
+            members = [cand[i] for i in range(len(cand)) if mask >> i & 1]
+            if sum(units[j] for j in members) <= budget:
+                best = max(best, len(members))
+        k = oracle.coverage_budget_row(s, L, W, ns, tau)
+        assert k == L - best, (tau, k, best)
+        row = oracle.select(s[None, None], L, W, ns, tau=tau)[0, 0]
+        assert row[:k].tolist() == oracle.select_row(s, k, W, ns).tolist()
+        assert (row[k:] == -1).all()
+        dropped = sorted(set(range(L)) - set(row[:k].tolist()))
+        assert sum(units[j] for j in dropped) <= budget
+
+
+def test_coverage_limits_and_monotone():
+    rng = np.random.default_rng(3)
+    L, W, ns = 200, 8, 4
+    s = rng.random(L) + 2.0 ** -30                 # every score at least one unit
+    assert oracle.coverage_budget_row(s, L, W, ns, 1e-30) == L            # budget 0: nobody leaves
+    assert oracle.coverage_budget_row(s, L, W, ns, 1.0) == ns + W         # everything non-forced leaves
+    ks = [oracle.coverage_budget_row(s, L, W, ns, t) for t in (1e-6, 1e-4, 1e-3, 0.01, 0.05, 0.2, 0.5, 0.9)]
+    assert all(a >= b for a, b in zip(ks, ks[1:])) and ks[0] > ks[-1]
+    # zero-mass positions (below one unit) leave even with a zero budget
+    z = s.copy()
+    z[[20, 30, 40]] = 2.0 ** -45
+    assert oracle.coverage_budget_row(z, L, W, ns, 1e-30) == L - 3
+
+
+def test_coverage_uniform_closed_form():
+    # All candidates score x: floor(budget / units(x)) of them leave (at most all of them).
+    L, W, ns = 100, 4, 2
+    for x, tau in ((0.75, 0.05), (0.3, 0.013), (1.0, 0.5)):
+        s = np.full(L, x)
+        u = oracle.mass_units([x])[0]
+        budget = math.floor(float(np.float32(tau)) * float(u * L))
+        n_cand = L - ns - W
+        assert oracle.coverage_budget_row(s, L, W, ns, tau) == L - min(n_cand, budget // u)
+        # ties leave from the highest position down: the kept candidates are the lowest ones
+        k = oracle.coverage_budget_row(s, L, W, ns, tau)
+        row = oracle.select(s[None, None], L, W, ns, tau=tau)[0, 0, :k]
+        assert row.tolist() == list(range(k - W)) + list(range(L - W, L))
+
+
+def test_coverage_group_rows_and_padding_through_stages():
+    # Per KV head the budget is taken on the summed rows; padded idx entries give zero
+    # gathered rows and are skipped by the scatter, and valid compact rows never see them.
+    x = workloads.small_random(1, 4, 2, 40, 8, seed=5, dtype="f32")
+    s = oracle.score(x["q"], x["k"], 8).astype(np.float32)
+    kv = oracle.coverage_budget(s, 40, 8, 2, 0.05, kv_heads=2)
+    gs = oracle.group_scores(s, 2)
+    assert kv.tolist() == [[oracle.coverage_budget_row(gs[0, g], 40, 8, 2, 0.05) for g in range(2)]]
+    idx = oracle.select(s, 30, 8, 2, tau=0.3)
+    qh, kh, vh = oracle.gather(x["q"], x["k"], x["v"], idx)
+    oh = oracle.attend(qh, kh, vh)
+    out = oracle.scatter_residual(oh, idx, x["r"])
+    ks = (idx[0] >= 0).sum(axis=1)
+    assert ks.min() < 30                           # the rule binds below the cap somewhere
+    for h in range(4):
+        k_h = int(ks[h])
+        assert np.all(qh[0, h, k_h:] == 0) and np.all(kh[0, h, k_h:] == 0)
+        sub = oracle.attend(qh[:, h:h + 1, :k_h], kh[:, h:h + 1, :k_h], vh[:, h:h + 1, :k_h])
+        np.testing.assert_allclose(oh[0, h, :k_h], sub[0, 0], rtol=1e-12, atol=1e-12)
+        rows = idx[0, h, :k_h]
+        others = np.setdiff1d(np.arange(40), rows)
+        assert np.array_equal(out[0, others, h], np.asarray(x["r"], dtype=np.float64)[0, others, h])
+        np.testing.assert_allclose(out[0, rows, h], x["r"][0, rows, h] + oh[0, h, :k_h], rtol=1e-12, atol=1e-12)
