@@ -21,11 +21,22 @@
  *   this library, not from the pages: the G query heads of KV head g share one subset
  *   S_g, chosen by the same rule on the sum of their G score rows, R = Hkv subsets).  Query
  *   head h uses subset r(h) = h / (H / R).
+ * Adaptive budgets (tsa_desc.tau > 0): the paper page lets per-head budgets adapt through
+ *   a token coverage tau (TL;DR; Figures 1 and 5: higher is sparser) and gives no formula.
+ *   This library's rule, per subset row: non-forced positions leave in the reverse of the
+ *   keep order (lower score first, equal scores from the higher position) while the scores
+ *   that left add up to at most floor(tau * T), T the row's total score; every score
+ *   counts as a whole number of 2^-40 units, rounded down, so the sums are exact.  The
+ *   row keeps K_r = min(L - leavers, keep) positions (keep is the cap; K_r >= |F|).  idx
+ *   rows then hold K_r ascending positions followed by -1 padding up to keep.  tau = 0
+ *   disables the rule (every row keeps exactly keep positions).
  * Layouts (contiguous, row-major, element strides implied by the sizes):
  *   q, residual, out, o        [B][L][H][d]      (dtype)
  *   k, v                        [B][L][Hkv][d]    (dtype)
  *   scores                      [B][H][L]         (fp32, always per query head)
- *   idx                         [B][R][keep]      (int32, strictly ascending per subset)
+ *   idx                         [B][R][keep]      (int32, strictly ascending per subset;
+ *                                                  -1 padding past K_r when tau > 0)
+ *   counts                      [B][R]            (int32, K_r of every subset row)
  *   qh, oh                      [B][H][keep][d]   (dtype; compact per-query-head tensors)
  *   kh, vh                      [B][R][keep][d]   (dtype; compact K/V rows of each subset,
  *                                                  read from KV head g(h) of its heads)
@@ -52,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 2
+#define TSA_ABI_VERSION 3
 #define TSA_MAX_W 64 /* largest score window the scoring kernel holds in registers */
 
 typedef enum {
@@ -65,7 +76,8 @@ typedef enum {
   TSA_ERR_WORKSPACE = 6, /* ws_bytes smaller than tsa_workspace_size, or ws NULL when needed */
   TSA_ERR_ALIAS = 7,     /* an output overlaps an input it must not overlap */
   TSA_ERR_LAUNCH = 8,    /* a kernel launch failed */
-  TSA_ERR_ARG = 9        /* an enum argument (op, subsets) out of range, or scale not finite / negative */
+  TSA_ERR_ARG = 9        /* an enum argument (op, subsets) out of range, scale not finite / negative, or
+                            tau outside [0, 1] */
 } tsa_status;
 
 typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
@@ -84,6 +96,8 @@ typedef struct {
   int32_t dtype;  /* tsa_dtype */
   float scale;    /* logit scale; 0 selects 1/sqrt(d) */
   int32_t subsets; /* tsa_subsets */
+  float tau;       /* token coverage in [0, 1]: 0 = every subset keeps `keep` positions, > 0 = adaptive
+                      budgets capped at `keep` (see "Adaptive budgets") */
 } tsa_desc;
 
 /* Returns TSA_ABI_VERSION. */
@@ -122,11 +136,18 @@ tsa_status tsa_score(const tsa_desc* desc, const void* q, const void* k, float* 
 tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Adaptive budgets alone (paper page: TL;DR and Figures 1 and 5, token coverage; the rule
+ * is the library's reading, see "Adaptive budgets").  In: scores [B][H][L] (>= 0).  Out:
+ * counts [B][R], K_r of every subset row (keep everywhere when tau = 0), exactly the row
+ * lengths tsa_select produces.  Workspace: TSA_OP_SELECT. */
+tsa_status tsa_budget(const tsa_desc* desc, const float* scores, int32_t* counts,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Gather-compression (skill page, Step 2, gathering the selected tokens; Figure 3,
  * stage 1):  qh[b][h][t] = q[b][idx[b][r(h)][t]][h]; for each subset r, with g the KV
  * head of its query heads, kh[b][r][t] = k[b][idx[b][r][t]][g] and vh likewise.
- * Bit-exact copies.  idx entries must lie in [0, L).  The outputs must not overlap the
- * inputs or one another. */
+ * Bit-exact copies.  An idx entry outside [0, L) (the -1 padding of adaptive budgets)
+ * gives zero rows at t.  The outputs must not overlap the inputs or one another. */
 tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v,
                           const int32_t* idx, void* qh, void* kh, void* vh, void* stream);
 
@@ -135,14 +156,16 @@ tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, co
  *                 softmax_u( scale * <qh[b][h][t], kh[b][r(h)][u]> ) vh[b][r(h)][u],
  * fp32 accumulation and online softmax, result rounded once to dtype.  Because every
  * subset is ascending, the causal mask on compact rows equals the mask on original
- * positions.  oh must not overlap qh, kh or vh. */
+ * positions, and rows t < K_r never see the zero rows gathered for padding entries.  oh
+ * must not overlap qh, kh or vh. */
 tsa_status tsa_attn(const tsa_desc* desc, const void* qh, const void* kh, const void* vh,
                     void* oh, void* stream);
 
 /* Scatter-decompression plus residual (skill page, Step 2, scattering back to the full
  * sequence; Figure 3: scatter into the full layout, then add the residual):
  *   out[b][p][h] = residual[b][p][h] + oh[b][h][t]   if p = idx[b][r(h)][t],
- *   out[b][p][h] = residual[b][p][h]                 (bit-exact) otherwise.
+ *   out[b][p][h] = residual[b][p][h]                 (bit-exact) otherwise;
+ * idx entries outside [0, L) (padding) are skipped.
  * The sum is formed in fp32 and rounded once (round to nearest even).  out == residual
  * (exactly the same pointer) updates in place and touches only the kept rows; any other
  * overlap of out with residual, oh or idx is TSA_ERR_ALIAS.  Workspace: TSA_OP_SCATTER
@@ -155,7 +178,8 @@ tsa_status tsa_scatter_residual(const tsa_desc* desc, const void* oh, const int3
  * scatter + residual (the skill page's Core Concept compress/decompress sequence;
  * Figure 3, both stages).  scores_opt / idx_opt, when not NULL, receive the scores and
  * the subsets; otherwise they live in the workspace.  out may equal residual (in place).
- * Workspace: TSA_OP_FORWARD. */
+ * With tau > 0 the row budgets are taken first and the attention runs only the K_r rows
+ * of each subset.  Workspace: TSA_OP_FORWARD. */
 tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const void* v,
                        const void* residual, void* out, float* scores_opt, int32_t* idx_opt,
                        void* ws, size_t ws_bytes, void* stream);

@@ -10,13 +10,14 @@ from tests._lib import ensure_built
 tsa = ensure_built()
 L = tsa.lib()
 
-EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_check", "tsa_dense_attn", "tsa_forward", "tsa_gather_qkv",
+EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_budget", "tsa_check", "tsa_dense_attn", "tsa_forward",
+            "tsa_gather_qkv",
             "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_status_str", "tsa_workspace_size"]
 
 
 def D(**kw):
     base = dict(B=1, H=32, Hkv=8, L=8192, d=128, keep=4096, W=64, n_sink=4, dtype=tsa.TSA_BF16, scale=0.0,
-                subsets=tsa.TSA_SUBSETS_PER_HEAD)
+                subsets=tsa.TSA_SUBSETS_PER_HEAD, tau=0.0)
     base.update(kw)
     return tsa.make_desc(**base)
 
@@ -26,7 +27,7 @@ def test_header_declares_and_library_exports_every_entry_point():
     assert declared == EXPECTED
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tsa_abi_version() == 2
+    assert L.tsa_abi_version() == 3
     assert L.tsa_status_str(7) and L.tsa_status_str(1234) == b"unknown status"
 
 
@@ -47,6 +48,8 @@ def test_header_declares_and_library_exports_every_entry_point():
     (dict(B=4096, H=32), 2),                   # grid limit
     (dict(subsets=1), 0),                      # one subset per KV head
     (dict(subsets=2), 9), (dict(subsets=-1), 9),
+    (dict(tau=0.005), 0), (dict(tau=1.0), 0),  # adaptive budgets
+    (dict(tau=-0.1), 9), (dict(tau=1.5), 9), (dict(tau=float("nan")), 9),
 ])
 def test_check_codes(kw, code):
     assert tsa.tsa_check(D(**kw)) == code
@@ -76,6 +79,10 @@ def test_workspace_sizes():
     assert tsa.tsa_workspace_size(kv, tsa.TSA_OP_SCATTER) == 8 * 8192 * 4
     kv32 = tsa.tsa_workspace_size(D(dtype=tsa.TSA_F32, subsets=1), tsa.TSA_OP_FORWARD)
     assert 2 * 32 * 4096 * 128 * 4 + 2 * 8 * 4096 * 128 * 4 <= kv32 < fwd32
+    # adaptive budgets add 64-bit mass histograms to the select and the row budgets to the forward
+    ad = D(tau=0.01)
+    assert tsa.tsa_workspace_size(ad, tsa.TSA_OP_SELECT) >= tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) + 32 * 2048 * 8
+    assert tsa.tsa_workspace_size(ad, tsa.TSA_OP_FORWARD) > fwd
 
 
 A = 1 << 40           # fake, well-separated, 16-byte aligned addresses
@@ -124,6 +131,12 @@ def test_entry_points_reject_before_launch():
     assert call("tsa_select", bd, sc, idx, None, 0, None) == 6
     assert call("tsa_select", bd, sc, idx, ws, 16, None) == 6
     assert call("tsa_select", bd, sc, idx, idx + 64, big, None) == 7
+    assert call("tsa_budget", bd, sc, None, ws, big, None) == 1
+    assert call("tsa_budget", bd, sc, idx, None, 0, None) == 6
+    assert call("tsa_budget", bd, sc, idx + 4, ws, big, None) == 5
+    assert call("tsa_budget", bd, sc, sc + 64, ws, big, None) == 7
+    assert call("tsa_budget", bd, sc, idx, sc + 4096, big, None) == 7
+    assert call("tsa_budget", ctypes.byref(D(tau=2.0)), sc, idx, ws, big, None) == 9
     kvd = ctypes.byref(D(subsets=tsa.TSA_SUBSETS_PER_KV_HEAD))
     assert call("tsa_select", kvd, sc, idx, None, 0, None) == 6
     assert call("tsa_select", kvd, sc, idx, ws, 8 * 8192 * 4, None) == 6

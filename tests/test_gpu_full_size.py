@@ -25,7 +25,7 @@ _CACHE = {}
 
 def _inputs(name):
     w = workloads.WORKLOADS[name]
-    key = (w.B, w.L, w.H, w.Hkv, w.d, w.dtype, w.planted, w.seed)
+    key = (w.B, w.L, w.H, w.Hkv, w.d, w.dtype, w.planted, w.seed, w.q_grade)
     if key not in _CACHE:
         _CACHE.clear()
         _CACHE[key] = workloads.make_inputs(w)
@@ -168,5 +168,49 @@ def test_full_per_kv_head_L128k():
             worst_out = max(worst_out, float((np.abs(got - want) - half_ulp(got, w.dtype)).max()))
     print(f"{w.name} per KV head: score rel err {worst_s:.2e}, out excess {worst_out:.2e}, "
           f"subset differences {n_diff}")
+    assert worst_s <= 1e-5
+    assert worst_out <= TOL[w.dtype]
+
+
+def test_full_adaptive_graded_L128k():
+    # Adaptive budgets (token coverage 0.2, no cap below L) at L = 131072 through
+    # tsa_forward (bf16 fused), heads graded from diffuse to concentrated attention.
+    w, x = _inputs("bf16_L128k_tau0.2_graded")
+    dt = torch.bfloat16
+    q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
+    out, sg, ig = tsa.forward(q, k, v, r, w.keep, w.W, w.n_sink, return_scores=True, tau=w.tau)
+    torch.cuda.synchronize()
+    B, L, H, d = x["q"].shape
+    G = H // w.Hkv
+    scale = 1.0 / np.sqrt(d)
+    s32 = sg.cpu().numpy()
+    idx_all = ig.cpu().numpy().astype(np.int64)
+    # budgets and subsets of every head bit-exact on the GPU's own scores
+    assert np.array_equal(idx_all, oracle.select(s32, w.keep, w.W, w.n_sink, tau=w.tau))
+    ks = (idx_all >= 0).sum(axis=-1)
+    print(f"{w.name}: K/L per head {ks.min() / L:.3f} .. {ks.max() / L:.3f}, mean {ks.mean() / L:.3f}")
+    assert ks[0, 0] > ks[0, -1]                    # sharper heads keep fewer positions
+    sel = torch.zeros(B, H, L + 1, dtype=torch.bool, device="cuda")
+    sel.scatter_(2, torch.where(ig >= 0, ig, L).long(), True)
+    sel = sel[:, :, :L].permute(0, 2, 1)
+    assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16))
+    assert int(sel.sum()) == int(ks.sum())
+    rng = np.random.default_rng(4)
+    worst_s, worst_out = 0.0, 0.0
+    for b, h in [(0, 0), (0, 31)]:
+        g = h // G
+        qh = x["q"][b, :, h, :].astype(np.float64)
+        kg = x["k"][b, :, g, :].astype(np.float64)
+        vg = x["v"][b, :, g, :].astype(np.float64)
+        worst_s = max(worst_s, rel_err(s32[b, h].astype(np.float64), oracle.score_head(qh, kg, w.W, scale)))
+        kh_ = int(ks[b, h])
+        idx = idx_all[b, h, :kh_]
+        rows = np.unique(np.concatenate([[0, kh_ - 1], rng.integers(0, kh_, 8)]))
+        o_rows = oracle.attend_rows(qh[idx], kg[idx], vg[idx], rows, scale)
+        pos = idx[rows]
+        got = out[b, torch.from_numpy(pos).cuda(), h, :].float().cpu().numpy().astype(np.float64)
+        want = x["r"][b, pos, h, :].astype(np.float64) + o_rows
+        worst_out = max(worst_out, float((np.abs(got - want) - half_ulp(got, w.dtype)).max()))
+    print(f"{w.name}: score rel err {worst_s:.2e}, out excess {worst_out:.2e}")
     assert worst_s <= 1e-5
     assert worst_out <= TOL[w.dtype]

@@ -30,7 +30,7 @@ TSA_OK = 0
 TSA_F32, TSA_BF16 = 0, 1
 TSA_OP_SCORE, TSA_OP_SELECT, TSA_OP_SCATTER, TSA_OP_FORWARD = 0, 1, 2, 3
 TSA_SUBSETS_PER_HEAD, TSA_SUBSETS_PER_KV_HEAD = 0, 1
-ABI_VERSION = 2   # TSA_ABI_VERSION of include/tsa.h that this binding's TsaDesc matches
+ABI_VERSION = 3   # TSA_ABI_VERSION of include/tsa.h that this binding's TsaDesc matches
 STATUS_NAMES = {0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_SHAPE", 3: "TSA_ERR_BUDGET", 4: "TSA_ERR_DTYPE",
                 5: "TSA_ERR_ALIGN", 6: "TSA_ERR_WORKSPACE", 7: "TSA_ERR_ALIAS", 8: "TSA_ERR_LAUNCH", 9: "TSA_ERR_ARG"}
 
@@ -38,7 +38,8 @@ STATUS_NAMES = {0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_SHAPE", 3: "TSA_ERR_
 class TsaDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("keep", ctypes.c_int32), ("W", ctypes.c_int32), ("n_sink", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("subsets", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("subsets", ctypes.c_int32),
+                ("tau", ctypes.c_float)]
 
     def __repr__(self):
         return "TsaDesc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -61,6 +62,7 @@ _SIGS = {
     "tsa_workspace_size": ([_DP, ctypes.c_int, ctypes.POINTER(_SZ)], ctypes.c_int),
     "tsa_score": ([_DP, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_select": ([_DP, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "tsa_budget": ([_DP, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_gather_qkv": ([_DP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "tsa_attn": ([_DP, _P, _P, _P, _P, _P], ctypes.c_int),
     "tsa_scatter_residual": ([_DP, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -95,10 +97,11 @@ def header_functions() -> list[str]:
 
 # ---- descriptors and marshalling ------------------------------------------------------
 
-def make_desc(B, H, Hkv, L, d, keep, W, n_sink, dtype, scale: float = 0.0, subsets: int = 0) -> TsaDesc:
+def make_desc(B, H, Hkv, L, d, keep, W, n_sink, dtype, scale: float = 0.0, subsets: int = 0,
+              tau: float = 0.0) -> TsaDesc:
     code = {torch.float32: TSA_F32, torch.bfloat16: TSA_BF16}.get(dtype, dtype)
     return TsaDesc(int(B), int(H), int(Hkv), int(L), int(d), int(keep), int(W), int(n_sink), int(code), float(scale),
-                   int(subsets))
+                   int(subsets), float(tau))
 
 
 def _ptr(t) -> int | None:
@@ -140,6 +143,10 @@ def tsa_score(desc, q, k, scores, ws, ws_bytes=None, stream=None):
 
 def tsa_select(desc, scores, idx, ws=None, ws_bytes=0, stream=None):
     _call("tsa_select", ctypes.byref(desc), _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def tsa_budget(desc, scores, counts, ws=None, ws_bytes=0, stream=None):
+    _call("tsa_budget", ctypes.byref(desc), _ptr(scores), _ptr(counts), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def tsa_gather_qkv(desc, q, k, v, idx, qh, kh, vh, stream=None):
@@ -185,11 +192,11 @@ def _check_io(q, k, v=None):
         raise ValueError("q must be [B, L, H, d] and k, v [B, L, Hkv, d]")
 
 
-def desc_for(q, k, keep, W=64, n_sink=4, scale=0.0, per_kv_head=False) -> TsaDesc:
+def desc_for(q, k, keep, W=64, n_sink=4, scale=0.0, per_kv_head=False, tau=0.0) -> TsaDesc:
     B, L, H, d = q.shape
     keep = min(int(keep), L)   # a budget larger than the sequence keeps everything
     return make_desc(B, H, k.shape[2], L, d, keep, W, n_sink, q.dtype, scale,
-                     TSA_SUBSETS_PER_KV_HEAD if per_kv_head else TSA_SUBSETS_PER_HEAD)
+                     TSA_SUBSETS_PER_KV_HEAD if per_kv_head else TSA_SUBSETS_PER_HEAD, tau)
 
 
 def _workspace(desc, op, device):
@@ -206,20 +213,34 @@ def score(q, k, W=64, scale=0.0):
     return scores
 
 
-def select(scores, keep, W=64, n_sink=4, kv_heads=None):
-    """idx [B, R, keep] (int32, ascending) from scores [B, H, L]: one subset per query head
-    (R = H), or with kv_heads=Hkv one per KV head on the summed scores of its heads."""
+def _select_desc(scores, keep, W, n_sink, kv_heads, tau):
     if not scores.is_cuda or scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous float32 GPU tensor")
     B, H, L = scores.shape
-    keep = min(int(keep), L)
     R = H if kv_heads is None else int(kv_heads)
-    desc = make_desc(B, H, R, L, 128, keep, W, n_sink, TSA_F32, 0.0,
-                     TSA_SUBSETS_PER_HEAD if kv_heads is None else TSA_SUBSETS_PER_KV_HEAD)
-    idx = torch.empty(B, R, keep, dtype=torch.int32, device=scores.device)
+    return make_desc(B, H, R, L, 128, min(int(keep), L), W, n_sink, TSA_F32, 0.0,
+                     TSA_SUBSETS_PER_HEAD if kv_heads is None else TSA_SUBSETS_PER_KV_HEAD, tau), R
+
+
+def select(scores, keep, W=64, n_sink=4, kv_heads=None, tau=0.0):
+    """idx [B, R, keep] (int32, ascending) from scores [B, H, L]: one subset per query head
+    (R = H), or with kv_heads=Hkv one per KV head on the summed scores of its heads.  With
+    tau > 0 each row holds its adaptive budget of positions, then -1 padding."""
+    desc, R = _select_desc(scores, keep, W, n_sink, kv_heads, tau)
+    idx = torch.empty(desc.B, R, desc.keep, dtype=torch.int32, device=scores.device)
     ws = _workspace(desc, TSA_OP_SELECT, scores.device)
     tsa_select(desc, scores, idx, ws, ws.numel())
     return idx
+
+
+def budget(scores, keep, W=64, n_sink=4, kv_heads=None, tau=0.0):
+    """counts [B, R] (int32): the positions each subset row keeps under token coverage tau
+    (capped at keep; keep everywhere when tau = 0)."""
+    desc, R = _select_desc(scores, keep, W, n_sink, kv_heads, tau)
+    counts = torch.empty(desc.B, R, dtype=torch.int32, device=scores.device)
+    ws = _workspace(desc, TSA_OP_SELECT, scores.device)
+    tsa_budget(desc, scores, counts, ws, ws.numel())
+    return counts
 
 
 def gather_qkv(q, k, v, idx):
@@ -262,11 +283,11 @@ def scatter_residual(oh, idx, residual, out=None):
 
 
 def forward(q, k, v, residual, keep, W=64, n_sink=4, scale=0.0, out=None, return_scores=False, ws=None,
-            per_kv_head=False):
+            per_kv_head=False, tau=0.0):
     """One token-sparse attention layer: returns out (and scores [B, H, L], idx [B, R, keep]
-    when asked)."""
+    when asked).  tau > 0: adaptive budgets capped at keep."""
     _check_io(q, k, v)
-    desc = desc_for(q, k, keep, W, n_sink, scale, per_kv_head)
+    desc = desc_for(q, k, keep, W, n_sink, scale, per_kv_head, tau)
     if out is None:
         out = torch.empty_like(residual)
     if ws is None:

@@ -39,6 +39,7 @@ tsa_status check_shape(const tsa_desc* d) {
   if (d->H % d->Hkv != 0) return TSA_ERR_SHAPE;
   if (d->d != 64 && d->d != 128) return TSA_ERR_SHAPE;
   if (!std::isfinite(d->scale) || d->scale < 0.f) return TSA_ERR_ARG;
+  if (!(d->tau >= 0.f && d->tau <= 1.f)) return TSA_ERR_ARG;   // also rejects NaN
   if (d->subsets != TSA_SUBSETS_PER_HEAD && d->subsets != TSA_SUBSETS_PER_KV_HEAD) return TSA_ERR_ARG;
   // Index limits of the launch grids (grid.y = B*H, 32-bit thread indices per batch entry).
   if ((int64_t)d->B * d->H > 65535) return TSA_ERR_SHAPE;
@@ -96,7 +97,7 @@ tsa_status after_launch(hipError_t e, hipStream_t s) {
 // Byte sizes of the tensors of a descriptor (idx, inv and the compact K/V have one row
 // per subset: H of them per head, Hkv per KV head; sel is the workspace of the select).
 struct Sizes {
-  size_t q, kv, scores, idx, compact, kvc, inv, sel, part, stat;
+  size_t q, kv, scores, idx, compact, kvc, inv, sel, part, stat, counts;
 };
 
 Sizes sizes_of(const tsa_desc& d) {
@@ -111,6 +112,7 @@ Sizes sizes_of(const tsa_desc& d) {
   z.kvc = (size_t)d.B * R * d.keep * d.d * e;
   z.inv = (size_t)d.B * R * d.L * 4;
   z.sel = tsa::select_layout(d).total;
+  z.counts = (size_t)d.B * R * 4;
   int chunk = 32, nchunk = 1;
   if (d.L > 0) tsa::score_chunking(d, chunk, nchunk);
   z.part = (size_t)d.B * d.H * nchunk * window(d) * 8;
@@ -122,7 +124,7 @@ Sizes sizes_of(const tsa_desc& d) {
 // bf16 forward is fused (attention reads the rows through idx and writes residual + O), so
 // it needs no compact tensors; the fp32 forward runs the stages one after the other.
 struct FwdLayout {
-  size_t scores, idx, inv, sel, part, stat, qh, kh, vh, oh, total;
+  size_t scores, idx, inv, sel, part, stat, counts, qh, kh, vh, oh, total;
 };
 
 FwdLayout fwd_layout(const tsa_desc& d) {
@@ -137,6 +139,7 @@ FwdLayout fwd_layout(const tsa_desc& d) {
   f.sel = o; o += round_up(z.sel);
   f.part = o; o += round_up(z.part);
   f.stat = o; o += round_up(z.stat);
+  f.counts = o; o += d.tau > 0.f ? round_up(z.counts) : 0;
   f.qh = o; o += comp;
   f.kh = o; o += kvc;
   f.vh = o; o += kvc;
@@ -220,7 +223,23 @@ tsa_status tsa_select(const tsa_desc* desc, const float* scores, int32_t* idx, v
   if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (overlap({ws, need}, {scores, z.scores}) || overlap({ws, need}, {idx, z.idx})) return TSA_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(tsa::launch_select(d, scores, idx, nullptr, ws, s), s);
+  return after_launch(tsa::launch_select(d, scores, idx, nullptr, nullptr, ws, s), s);
+}
+
+tsa_status tsa_budget(const tsa_desc* desc, const float* scores, int32_t* counts, void* ws, size_t ws_bytes,
+                      void* stream) {
+  TSA_TRY(check_full(desc));
+  const tsa_desc& d = *desc;
+  if (empty_problem(d)) return TSA_OK;
+  if (!scores || !counts) return TSA_ERR_NULL;
+  if (!aligned(scores) || !aligned(counts) || !aligned(ws)) return TSA_ERR_ALIGN;
+  const Sizes z = sizes_of(d);
+  if (overlap({scores, z.scores}, {counts, z.counts})) return TSA_ERR_ALIAS;
+  const size_t need = round_up(z.sel);
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (overlap({ws, need}, {scores, z.scores}) || overlap({ws, need}, {counts, z.counts})) return TSA_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(tsa::launch_budget(d, scores, counts, ws, s), s);
 }
 
 tsa_status tsa_gather_qkv(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -312,13 +331,14 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   void* oh = at<char>(ws, f.oh);
   const bool in_place = out == residual;
   TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
-  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, at<char>(ws, f.sel), s), s));
+  int32_t* counts = d.tau > 0.f ? at<int32_t>(ws, f.counts) : nullptr;
+  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, counts, at<char>(ws, f.sel), s), s));
   if (fused_forward(d)) {
     // Rows a head does not keep are the residual (copied out of place, untouched in place);
     // the attention epilogue writes residual + O into the kept rows.
     if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
     if (d.keep == 0) return TSA_OK;
-    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, residual, out, s), s);
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, residual, out, s), s);
   }
   if (d.keep > 0) {
     TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));

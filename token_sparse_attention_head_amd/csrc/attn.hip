@@ -55,6 +55,7 @@ struct AttnParams {
   const int32_t* idx;      // fused forward: [B][H / idx_div][n] positions of each subset's rows
   int idx_div;             // query heads per subset: head h reads idx row b * (H / idx_div) + h / idx_div
   const void* res;         // fused forward: residual, same layout as o
+  const int32_t* counts;   // fused forward with adaptive budgets: rows of each subset [B][H / idx_div], or NULL
 };
 
 constexpr int ATT_COMPACT = 0, ATT_DENSE = 1, ATT_FUSED = 2;
@@ -357,7 +358,6 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
 
   // Arguments in registers (lambdas capture by reference; a captured argument struct
   // would be placed in scratch memory).
-  const int n = p.n;
   const int64_t q_r = STRIDED ? p.q_r : D, k_r = STRIDED ? p.k_r : D, o_r = STRIDED ? p.o_r : D;
   const int kv_div = p.kv_div;
   const float c = p.c;
@@ -367,10 +367,19 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const int lane = lane_id();
   const int hf = lane >> 5, lc = lane & 31;
 
-  int bh, tile;
+  int bh, tile, n = p.n;
   {
     const int bid = blockIdx.x;
-    if (p.BH % 8 == 0) {
+    if (FUSED && p.counts) {
+      // Rows differ per subset: rank r of every head in turn (longest tiles first), heads
+      // rotated so that one head's tiles spread over all XCDs and none idles while
+      // another still holds a long head.
+      const int r = bid / p.BH;
+      bh = (bid % p.BH + r) % p.BH;
+      n = p.counts[(bh / p.H) * (p.H / p.idx_div) + (bh % p.H) / p.idx_div];
+      tile = (n + BM - 1) / BM - 1 - r;
+      if (tile < 0) return;
+    } else if (p.BH % 8 == 0) {
       const int hpx = p.BH / 8;
       const int x = bid % 8, sl = bid / 8;
       bh = x * hpx + sl / p.ntiles;
@@ -667,10 +676,10 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
 }
 
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             const void* res, void* out, hipStream_t s) {
+                             const int32_t* counts, const void* res, void* out, hipStream_t s) {
   if (d.dtype != TSA_BF16) return hipErrorInvalidValue;
   AttnParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res;
+  p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res; p.counts = counts;
   p.idx_div = heads_per_subset(d);
   p.n = d.keep;
   p.H = d.H;

@@ -19,22 +19,28 @@ hipError_t launch_score(const tsa_desc& d, const void* q, const void* k, float* 
                         hipStream_t s);
 // Workspace of the select (each region 256-byte aligned): the summed score rows of a
 // KV group (subsets per KV head only), the per-row state of the radix select, the
-// per-row global histograms and the per-wave counts of the compaction.  S position
-// slices of seg positions per row.
+// per-row global histograms and the per-wave counts of the compaction; with adaptive
+// budgets (tau > 0) also the per-row mass histograms, the budget state and the row
+// budgets.  S position slices of seg positions per row.
 struct SelectLayout {
-  size_t gsum, state, hist, counts, total;
+  size_t gsum, state, hist, counts, mhist, bstate, budgets, total;
   int S, seg;
 };
 SelectLayout select_layout(const tsa_desc& d);
-hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, void* ws,
-                         hipStream_t s);
+// Row budgets [B][R]: keep for every row, or the token-coverage budget when tau > 0.
+hipError_t launch_budget(const tsa_desc& d, const float* scores, int32_t* counts, void* ws, hipStream_t s);
+// Subsets into idx (rows padded with -1 below keep when tau > 0) and optionally the inverse
+// map; with tau > 0 the row budgets go to `budgets` (NULL: the workspace).
+hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, int32_t* inv, int32_t* budgets,
+                         void* ws, hipStream_t s);
 hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              void* qh, void* kh, void* vh, hipStream_t s);
 hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh, const void* vh, void* oh,
                                hipStream_t s);
 // Fused forward attention (bf16): compact rows read through idx, out rows = residual + O.
+// counts (NULL: keep rows everywhere) gives each subset's row count under adaptive budgets.
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             const void* res, void* out, hipStream_t s);
+                             const int32_t* counts, const void* res, void* out, hipStream_t s);
 // Copies residual to out at the positions a head does not keep (inverse map < 0).
 hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s);
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,

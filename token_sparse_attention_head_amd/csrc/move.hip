@@ -37,6 +37,15 @@ __global__ __launch_bounds__(256) void gather_qkv_kernel(const char* __restrict_
   const int Hkv = H / G;
   const int64_t srow = (b * (H / SG) + h / SG) * keep + t;   // row of the subset
   const int p = idx[srow];
+  if ((unsigned)p >= (unsigned)L) {
+    // Padding entry (-1 past a row's adaptive budget): zero rows.
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st16(qh + ((int64_t)bh * keep + t) * ROWB + c * 16, z);
+    if (h % SG != 0) return;
+    st16(kh + srow * ROWB + c * 16, z);
+    st16(vh + srow * ROWB + c * 16, z);
+    return;
+  }
   const int64_t qoff = ((b * L + p) * H + h) * ROWB + c * 16;
   st16(qh + ((int64_t)bh * keep + t) * ROWB + c * 16, ld16(q + qoff));
   if (h % SG != 0) return;
@@ -104,6 +113,7 @@ __global__ __launch_bounds__(256) void scatter_add_inplace_kernel(const char* __
   const int64_t b = bh / H;
   const int64_t crow = (int64_t)bh * keep + t;
   const int p = idx[(b * (H / SG) + h / SG) * keep + t];
+  if ((unsigned)p >= (unsigned)L) return;       // padding entry
   char* dst = out + ((b * L + p) * H + h) * ROWB + c * 16;
   st16(dst, add_rows(ld16(dst), ld16(oh + crow * ROWB + c * 16), DT));
 }
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(256) void invert_kernel(const int32_t* __restrict__
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= keep) return;
   const int p = idx[(int64_t)bh * keep + t];
-  inv[(int64_t)bh * L + p] = t;
+  if ((unsigned)p < (unsigned)L) inv[(int64_t)bh * L + p] = t;   // padding entries map nothing
 }
 
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }

@@ -21,6 +21,11 @@ Recipe (device independent, reproducible on any host):
   forms the unit direction u of the mean of the last 64 queries of the heads in that
   KV group, and replaces each picked key by ``4 * |k| * u`` (then rounds to bf16).
   Picked tokens are never in the forced set, so only the scores can select them.
+* Graded workloads (``q_grade`` > 1) multiply the float32 queries of head h by
+  ``1 + (q_grade - 1) * h / (H - 1)`` before rounding, so the heads range from diffuse
+  to concentrated attention (sharper logits) and adaptive budgets differ per head.
+  N(0,1) draws alone give nearly uniform token scores, unlike the concentrated attention
+  of trained models that token coverage is meant for.
 
 The long-context workloads stand in for the long-context benchmark suites the paper
 evaluates on (the pages give sequence lengths, not data): N(0,1) activations with
@@ -54,6 +59,8 @@ class Workload:
     dtype: str  # "fp32" or "bf16"
     planted: bool = False
     seed: int = 0
+    tau: float = 0.0      # token coverage of adaptive budgets (0: every subset keeps `keep`)
+    q_grade: float = 1.0  # query scale of the last head (graded workloads)
 
     @property
     def G(self) -> int:
@@ -84,6 +91,10 @@ WORKLOADS = {
     # Skewed importance: 1% planted keys per KV head, two batch entries.
     "bf16_L64k_planted": Workload("bf16_L64k_planted", 2, 32, 8, 65536, 128, _keep(0.1, 65536), 64, 4, "bf16",
                                   planted=True),
+    # Adaptive budgets: token coverage 0.2, no cap below L, heads graded from diffuse to
+    # concentrated (query scale 1 .. 4).
+    "bf16_L128k_tau0.2_graded": Workload("bf16_L128k_tau0.2_graded", 1, 32, 8, 131072, 128, 131072, 64, 4, "bf16",
+                                         tau=0.2, q_grade=4.0),
 }
 
 
@@ -146,6 +157,8 @@ def make_inputs(w: Workload) -> dict:
     the workload plants keys.
     """
     q = _draw(0, (w.B, w.L, w.H, w.d), w.seed)
+    if w.q_grade != 1.0 and w.H > 1:
+        q *= (1.0 + (w.q_grade - 1.0) * np.arange(w.H, dtype=np.float32) / (w.H - 1))[None, None, :, None]
     k = _draw(1, (w.B, w.L, w.Hkv, w.d), w.seed)
     v = _draw(2, (w.B, w.L, w.Hkv, w.d), w.seed)
     r = _draw(3, (w.B, w.L, w.H, w.d), w.seed)
@@ -167,7 +180,7 @@ def make_inputs(w: Workload) -> dict:
     return {"q": q, "k": k, "v": v, "r": r, "planted": planted}
 
 
-def small_random(B, H, Hkv, L, d, seed=0, dtype="fp32") -> dict:
+def small_random(B, H, Hkv, L, d, seed=0, dtype="fp32", q_grade=1.0) -> dict:
     """Small seeded inputs of any shape (test cases); same recipe as ``make_inputs``."""
-    w = Workload("adhoc", B, H, Hkv, L, d, L, 1, 0, dtype, seed=seed)
+    w = Workload("adhoc", B, H, Hkv, L, d, L, 1, 0, dtype, seed=seed, q_grade=q_grade)
     return make_inputs(w)
