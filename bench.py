@@ -19,6 +19,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -176,6 +178,53 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     return res
 
 
+def adaptive_case(tsa, torch, timer, w, steps, reps, dense_ms):
+    """The layer under adaptive budgets (token coverage w.tau, cap w.keep) on a graded
+    workload: step time, the spread of the row budgets, the attention work they imply
+    (sum over heads of 2*d*K_h*(K_h+1)), and a fixed-budget step with the same total
+    attention work spread evenly (keep = sqrt(mean K_h*(K_h+1))), which shows what the
+    uneven rows cost."""
+    import math
+    import workloads
+    log(f"generating inputs for {w.name}")
+    x = workloads.make_inputs(w)
+    q, k, v, r = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkvr")
+    del x
+    B, L, H, D = q.shape
+    desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink, tau=w.tau)
+    ws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(r)
+    scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    step = lambda: tsa.tsa_forward(desc, q, k, v, r, out, None, None, ws)   # noqa: E731
+    step()
+    ms = timer.run(step, steps)
+    tsa.tsa_forward(desc, q, k, v, r, out, scores, None, ws)
+    counts = torch.empty(B, H, dtype=torch.int32, device="cuda")
+    lws = torch.empty(tsa.tsa_workspace_size(desc, tsa.TSA_OP_SELECT), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(B, H, w.keep, dtype=torch.int32, device="cuda")
+    budget_ms = timer.run(lambda: tsa.tsa_budget(desc, scores, counts, lws, lws.numel()), reps)
+    select_ms = timer.run(lambda: tsa.tsa_select(desc, scores, idx, lws, lws.numel()), reps)
+    K = counts.cpu().numpy().astype(np.float64)
+    flops = float(np.sum(2.0 * D * K * (K + 1)))
+    k_eq = int(round(math.sqrt(float(np.mean(K * (K + 1))))))
+    fdesc = tsa.desc_for(q, k, k_eq, w.W, w.n_sink)
+    fws = torch.empty(tsa.tsa_workspace_size(fdesc, tsa.TSA_OP_FORWARD), dtype=torch.uint8, device="cuda")
+    fstep = lambda: tsa.tsa_forward(fdesc, q, k, v, r, out, None, None, fws)   # noqa: E731
+    fstep()
+    fixed_ms = timer.run(fstep, steps)
+    res = {"workload": w.name, "subsets": "per_head_adaptive", "tau": w.tau, "keep_cap": w.keep,
+           "ms_per_step": ms, "tokens_per_s": B * L / (ms / 1e3),
+           "keep_ratio_per_head": {"min": K.min() / L, "mean": K.mean() / L, "max": K.max() / L},
+           "attn_flops": flops, "attn_tflops_over_step": flops / (ms * 1e-3) / 1e12,
+           "stage_ms": {"budget": budget_ms, "select_adaptive": select_ms},
+           "fixed_budget_same_work": {"keep": k_eq, "ms_per_step": fixed_ms}}
+    if dense_ms:
+        res["dense_ms"] = dense_ms
+        res["speedup_vs_dense"] = dense_ms / ms
+    del q, k, v, r, ws, fws, out, scores
+    return res
+
+
 def stage_only(tsa, torch, timer, w, x, name, reps):
     """One forward to build the stage inputs, then only `name`, reps times.  `copy` is a
     plain 1 GiB device-to-device copy (torch), the reference for HBM byte counters."""
@@ -311,6 +360,12 @@ def main():
                 res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
             log(f"{wi.name} per KV head: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
             sweep.append(res)
+        # Adaptive budgets (token coverage) on heads graded from diffuse to concentrated.
+        wa = workloads.WORKLOADS["bf16_L128k_tau0.2_graded"]
+        res = adaptive_case(tsa, torch, timer, wa, max(3, args.steps // 2), args.stage_reps, head.get("dense_ms"))
+        log(f"{wa.name}: {res['ms_per_step']:.3f} ms/step, K/L {json.dumps(res['keep_ratio_per_head'])}, "
+            f"fixed budget with the same work {json.dumps(res['fixed_budget_same_work'])}")
+        sweep.append(res)
 
     a = algorithmic(w)
     attn_ms = head["stage_ms"]["attn"]
@@ -335,8 +390,7 @@ def main():
                    "W": w.W, "n_sink": w.n_sink, "parallelism": "single GPU"},
         "speedup_vs_dense": head.get("speedup_vs_dense"), "dense_ms": head.get("dense_ms"),
         "stage_ms": head["stage_ms"], "stage_rate": head["stage_rate"],
-        "sweep": [{k: v for k, v in s.items() if k not in ("stage_rate",)} | {"stage_rate": s["stage_rate"]}
-                  for s in sweep],
+        "sweep": sweep,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

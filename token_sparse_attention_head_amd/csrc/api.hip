@@ -124,7 +124,7 @@ Sizes sizes_of(const tsa_desc& d) {
 // bf16 forward is fused (attention reads the rows through idx and writes residual + O), so
 // it needs no compact tensors; the fp32 forward runs the stages one after the other.
 struct FwdLayout {
-  size_t scores, idx, inv, sel, part, stat, counts, qh, kh, vh, oh, total;
+  size_t scores, idx, inv, sel, part, stat, counts, plan, qh, kh, vh, oh, total;
 };
 
 FwdLayout fwd_layout(const tsa_desc& d) {
@@ -140,6 +140,7 @@ FwdLayout fwd_layout(const tsa_desc& d) {
   f.part = o; o += round_up(z.part);
   f.stat = o; o += round_up(z.stat);
   f.counts = o; o += d.tau > 0.f ? round_up(z.counts) : 0;
+  f.plan = o; o += d.tau > 0.f && fused_forward(d) ? round_up(tsa::attn_plan_bytes(d)) : 0;
   f.qh = o; o += comp;
   f.kh = o; o += kvc;
   f.vh = o; o += kvc;
@@ -338,7 +339,7 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
     // the attention epilogue writes residual + O into the kept rows.
     if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
     if (d.keep == 0) return TSA_OK;
-    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, residual, out, s), s);
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, f.plan), residual, out, s), s);
   }
   if (d.keep > 0) {
     TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));

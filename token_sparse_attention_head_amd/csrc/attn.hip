@@ -56,7 +56,75 @@ struct AttnParams {
   int idx_div;             // query heads per subset: head h reads idx row b * (H / idx_div) + h / idx_div
   const void* res;         // fused forward: residual, same layout as o
   const int32_t* counts;   // fused forward with adaptive budgets: rows of each subset [B][H / idx_div], or NULL
+  const int32_t* plan;     // with counts: the per-XCD head lists of attn_plan_kernel, or NULL
+  int plan_cap;            // heads per XCD list in the plan
 };
+
+// Plan of the fused attention under adaptive budgets (rows differ per head).  A head's
+// workgroups read that head's own rows, so they should share an XCD's L2 (one XCD, one
+// head at a time); the XCDs should get equal work.  Heads are sorted by attention work
+// (tiles * (tiles + 1) / 2, longest first; ties by head) and dealt to the 8 XCDs in
+// snake order (0..7, 7..0, ...).  Plan layout (int32): [0, 8) tiles per XCD, then per XCD
+// `cap` head entries (bh, first slot).  Slot s of XCD x runs tile (tiles - 1 - (s - first))
+// of the entry whose range holds s.
+constexpr int PLAN_MAX_HEADS = 4096;
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void attn_plan_kernel(const int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ plan, int BH, int H,
+                                                                 int idx_div, int BM, int cap) {
+  __shared__ unsigned long long key[PLAN_MAX_HEADS];
+  int n2 = 1;
+  while (n2 < BH) n2 <<= 1;
+  for (int i = threadIdx.x; i < n2; i += PLAN_THREADS) {
+    unsigned long long k = 0;
+    if (i < BH) {
+      const int n = counts[(i / H) * (H / idx_div) + (i % H) / idx_div];
+      const unsigned long long t = (unsigned long long)((n + BM - 1) / BM);
+      k = ((t * (t + 1) / 2) << 32) | (0xFFFFFFFFu - (unsigned)i);   // work, then lower head first
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  // Bitonic sort, descending.
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += PLAN_THREADS) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const unsigned long long a = key[i], b = key[j];
+          if (desc ? a < b : a > b) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x < 8) {
+    const int x = threadIdx.x;
+    int32_t* list = plan + 8 + x * cap * 2;
+    int first = 0, e = 0;
+    for (int round = 0; round * 8 < BH; ++round) {
+      const int pos = (round & 1) ? 7 - x : x;
+      const int rank = round * 8 + pos;
+      if (rank >= BH) continue;
+      const int bh = (int)(0xFFFFFFFFu - (unsigned)(key[rank] & 0xFFFFFFFFu));
+      const int n = counts[(bh / H) * (H / idx_div) + (bh % H) / idx_div];
+      list[2 * e] = bh;
+      list[2 * e + 1] = first;
+      first += (n + BM - 1) / BM;
+      ++e;
+    }
+    for (; e < cap; ++e) {            // unused entries start past the end
+      list[2 * e] = 0;
+      list[2 * e + 1] = first;
+    }
+    plan[x] = first;
+  }
+}
 
 constexpr int ATT_COMPACT = 0, ATT_DENSE = 1, ATT_FUSED = 2;
 constexpr int BN = 64;          // keys per tile
@@ -370,10 +438,23 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   int bh, tile, n = p.n;
   {
     const int bid = blockIdx.x;
-    if (FUSED && p.counts) {
-      // Rows differ per subset: rank r of every head in turn (longest tiles first), heads
-      // rotated so that one head's tiles spread over all XCDs and none idles while
-      // another still holds a long head.
+    if (FUSED && p.counts && p.plan) {
+      // Rows differ per subset: the XCD's head list from attn_plan_kernel, one head after
+      // another, longest tiles first.
+      const int x = bid % 8, sl = bid / 8;
+      if (sl >= p.plan[x]) return;
+      const int32_t* list = p.plan + 8 + x * p.plan_cap * 2;
+      int lo = 0, hi = p.plan_cap - 1;             // last entry whose first slot <= sl
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (list[2 * mid + 1] <= sl) lo = mid; else hi = mid - 1;
+      }
+      bh = list[2 * lo];
+      n = p.counts[(bh / p.H) * (p.H / p.idx_div) + (bh % p.H) / p.idx_div];
+      tile = (n + BM - 1) / BM - 1 - (sl - list[2 * lo + 1]);
+    } else if (FUSED && p.counts) {
+      // Too many heads for a plan: rank r of every head in turn (longest tiles first),
+      // heads rotated so that one head's tiles spread over all XCDs.
       const int r = bid / p.BH;
       bh = (bid % p.BH + r) % p.BH;
       n = p.counts[(bh / p.H) * (p.H / p.idx_div) + (bh % p.H) / p.idx_div];
@@ -627,7 +708,13 @@ hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW * 32;
   p.BH = B * H;
   p.ntiles = (p.n + BM - 1) / BM;
-  const int64_t blocks = (int64_t)p.BH * p.ntiles;
+  int64_t blocks = (int64_t)p.BH * p.ntiles;
+  if (MODE == ATT_FUSED && p.counts && p.plan) {
+    p.plan_cap = (p.BH + 7) / 8;
+    attn_plan_kernel<<<1, PLAN_THREADS, 0, s>>>(p.counts, const_cast<int32_t*>(p.plan), p.BH, p.H, p.idx_div, BM,
+                                                p.plan_cap);
+    blocks = 8ll * p.plan_cap * p.ntiles;
+  }
   attn_bf16_kernel<D, NW, MODE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -675,11 +762,17 @@ hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh
   return dispatch_attn<false>(d, p, s);
 }
 
+size_t attn_plan_bytes(const tsa_desc& d) {
+  const int64_t BH = (int64_t)d.B * d.H;
+  return BH <= PLAN_MAX_HEADS ? (size_t)(8 + 8 * ((BH + 7) / 8) * 2) * 4 : 0;
+}
+
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             const int32_t* counts, const void* res, void* out, hipStream_t s) {
+                             const int32_t* counts, int32_t* plan, const void* res, void* out, hipStream_t s) {
   if (d.dtype != TSA_BF16) return hipErrorInvalidValue;
   AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res; p.counts = counts;
+  p.plan = attn_plan_bytes(d) ? plan : nullptr;
   p.idx_div = heads_per_subset(d);
   p.n = d.keep;
   p.H = d.H;

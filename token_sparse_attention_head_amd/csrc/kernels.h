@@ -38,9 +38,12 @@ hipError_t launch_gather_qkv(const tsa_desc& d, const void* q, const void* k, co
 hipError_t launch_attn_compact(const tsa_desc& d, const void* qh, const void* kh, const void* vh, void* oh,
                                hipStream_t s);
 // Fused forward attention (bf16): compact rows read through idx, out rows = residual + O.
-// counts (NULL: keep rows everywhere) gives each subset's row count under adaptive budgets.
+// counts (NULL: keep rows everywhere) gives each subset's row count under adaptive budgets;
+// plan is a workspace of attn_plan_bytes(d) bytes for the per-XCD head lists (0 bytes: too
+// many heads for a plan, heads are then interleaved over the XCDs).
+size_t attn_plan_bytes(const tsa_desc& d);
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             const int32_t* counts, const void* res, void* out, hipStream_t s);
+                             const int32_t* counts, int32_t* plan, const void* res, void* out, hipStream_t s);
 // Copies residual to out at the positions a head does not keep (inverse map < 0).
 hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s);
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
