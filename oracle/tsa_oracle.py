@@ -44,6 +44,12 @@ what remains, capped at ``keep``.  Scores are counted in whole units of 2^-40 (e
 rounded down) so that the integer K_h is decided by exact integer sums.  Rows with
 K_h < keep are padded with -1 in idx; gather gives zero rows there and scatter skips them.
 
+Representation drift (``drift``, ``layer_stable``): the skill page's Step 4 measures how
+much a layer changes the hidden states as one minus the mean, over tokens, of the cosine
+between each token's normalised vector before and after the layer (each vector divided
+by the larger of its norm and 1e-12), and calls a layer stable once the mean of its last
+three drifts is below 0.1.
+
 Every function works in float64; bf16 and fp32 inputs widen to float64 exactly.
 The readings taken where the pages are silent (window, causality, ties, order, the
 residual everywhere, the GQA head map, scale 1/sqrt(head_dim)) are stated at each
@@ -59,6 +65,7 @@ __all__ = [
     "window", "forced_positions", "score", "score_head", "select", "select_row",
     "gather", "attend", "attend_rows", "scatter_residual", "forward", "threshold", "group_scores",
     "MASS_UNIT_BITS", "mass_units", "coverage_budget_row", "coverage_budget",
+    "NORMALIZE_EPS", "drift", "layer_stable",
 ]
 
 
@@ -326,3 +333,33 @@ def forward(q, k, v, r, keep: int, W: int, n_sink: int, scale: float | None = No
     oh = attend(qh, kh, vh, scale)
     out = scatter_residual(oh, idx, r)
     return {"scores": s, "idx": idx, "qh": qh, "kh": kh, "vh": vh, "oh": oh, "out": out}
+
+
+NORMALIZE_EPS = 1e-12
+
+
+def drift(h_before, h_after) -> float:
+    """1 - mean over tokens of <h_before_t / max(|h_before_t|, eps), h_after_t / max(|h_after_t|, eps)>
+    for [..., dim] hidden states (skill page, Step 4, the representation drift)."""
+    a = _f64(h_before)
+    b = _f64(h_after)
+    a = a.reshape(-1, a.shape[-1])
+    b = b.reshape(-1, b.shape[-1])
+    na = np.maximum(np.sqrt((a * a).sum(axis=1)), NORMALIZE_EPS)
+    nb = np.maximum(np.sqrt((b * b).sum(axis=1)), NORMALIZE_EPS)
+    cos = ((a / na[:, None]) * (b / nb[:, None])).sum(axis=1)
+    return float(1.0 - cos.mean())
+
+
+def layer_stable(drifts, window: int = 3, threshold: float = 0.1) -> list:
+    """For a sequence of per-layer drifts, whether each layer counts as stable: the mean of
+    the last ``window`` drifts seen so far (this one included) is below ``threshold``;
+    never before ``window`` drifts have been seen (skill page, Step 4)."""
+    out = []
+    for i in range(len(drifts)):
+        if i + 1 < window:
+            out.append(False)
+            continue
+        recent = drifts[i + 1 - window:i + 1]
+        out.append(sum(recent) / len(recent) < threshold)
+    return out

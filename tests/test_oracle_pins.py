@@ -443,3 +443,45 @@ def test_coverage_group_rows_and_padding_through_stages():
         others = np.setdiff1d(np.arange(40), rows)
         assert np.array_equal(out[0, others, h], np.asarray(x["r"], dtype=np.float64)[0, others, h])
         np.testing.assert_allclose(out[0, rows, h], x["r"][0, rows, h] + oh[0, h, :k_h], rtol=1e-12, atol=1e-12)
+
+
+# ---- representation drift (skill page, Step 4) -----------------------------------------
+
+def test_drift_closed_forms():
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal((3, 50, 64))
+    assert abs(oracle.drift(a, a)) < 1e-15                       # unchanged: cosine 1
+    assert abs(oracle.drift(a, 3.5 * a)) < 1e-15                 # positive rescaling does not count
+    assert abs(oracle.drift(a, -a) - 2.0) < 1e-15                # reversed: cosine -1
+    # orthogonal pairs: swap the two halves of a vector with one sign flipped
+    b = np.concatenate([-a[..., 32:], a[..., :32]], axis=-1)
+    assert abs(oracle.drift(a, b) - 1.0) < 1e-14
+    # hand case: cosines 0, 1 and 1/2 (a 60 degree angle) -> drift 1 - 1/2 = 0.5
+    h0 = np.array([[1.0, 0.0], [1.0, 1.0], [1.0, 0.0]])
+    h1 = np.array([[0.0, 2.0], [3.0, 3.0], [1.0, math.sqrt(3.0)]])
+    assert abs(oracle.drift(h0, h1) - 0.5) < 1e-15
+    # a zero vector is normalised to zero (the norm is clamped at 1e-12): its cosine is 0
+    z = np.zeros((2, 4))
+    z[1] = [1, 2, 3, 4]
+    assert abs(oracle.drift(z, np.ones((2, 4))) - (1 - (0 + 10 / (math.sqrt(30) * 2)) / 2)) < 1e-15
+    # tokens are weighted equally whatever their norms
+    big = np.array([[1000.0, 0.0], [0.0, 0.001]])
+    assert abs(oracle.drift(big, np.array([[1.0, 0.0], [1.0, 0.0]])) - 0.5) < 1e-15
+
+
+def test_drift_small_angle_and_torch_cosine():
+    # Against torch's own cosine_similarity (float64, with its eps far below these norms).
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((2, 30, 128))
+    b = a + 0.05 * rng.standard_normal(a.shape)
+    cos = F.cosine_similarity(torch.from_numpy(a), torch.from_numpy(b), dim=-1).numpy()
+    assert abs(oracle.drift(a, b) - (1.0 - cos.mean())) < 1e-14
+    assert 0 < oracle.drift(a, b) < 0.01
+
+
+def test_layer_stable_window_rule():
+    # not before three drifts; then the mean of the last three against 0.1
+    assert oracle.layer_stable([0.0, 0.0]) == [False, False]
+    d = [0.05, 0.05, 0.05, 0.3, 0.01, 0.01, 0.01, 0.1, 0.1, 0.1]
+    assert oracle.layer_stable(d) == [False, False, True, False, False, False, True, True, True, False]
+    assert oracle.layer_stable([0.2, 0.0, 0.05], window=2, threshold=0.1) == [False, False, True]
