@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--stage-reps", type=int, default=5)
-    p.add_argument("--stage", choices=["score", "select", "gather", "attn", "scatter", "dense", "forward", "copy"],
+    p.add_argument("--stage", choices=["score", "select", "gather", "attn", "scatter", "dense", "forward", "drift",
+                                       "copy"],
                    help="run only this stage (after one full forward to make its inputs) --stage-reps times; "
                         "for profiler runs")
     return p.parse_args()
@@ -108,6 +109,7 @@ def algorithmic(w, per_kv_head=False):
         "attn_flops": 2.0 * B * H * d * K * (K + 1),
         "scatter_bytes": 2 * B * L * H * d * e + B * H * K * d * e + 4 * B * H * L,
         "dense_flops": 2.0 * B * H * d * L * (L + 1),
+        "drift_bytes": 2 * B * L * H * d * e,          # both hidden-state tensors read once
     }
 
 
@@ -148,6 +150,11 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     for name, fn in stages.items():
         fn()
         stage_ms[name] = timer.run(fn, reps)
+    # Representation drift across the layer (residual in, out): a bandwidth-bound reduction.
+    dws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_DRIFT)), dtype=torch.uint8, device="cuda")
+    dval = torch.empty((), dtype=torch.float64, device="cuda")
+    tsa.tsa_drift(desc, r, out, dval, dws)
+    stage_ms["drift"] = timer.run(lambda: tsa.tsa_drift(desc, r, out, dval, dws), reps)
     # In-place scatter variant (out == residual touches only kept rows); on a copy.
     r2 = r.clone()
     stage_ms["scatter_inplace"] = timer.run(lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r2, r2), reps)
@@ -163,6 +170,7 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
         "gather_gbs": a["gather_bytes"] / (stage_ms["gather"] * 1e-3) / 1e9,
         "attn_tflops": a["attn_flops"] / (stage_ms["attn"] * 1e-3) / 1e12,
         "scatter_gbs": a["scatter_bytes"] / (stage_ms["scatter"] * 1e-3) / 1e9,
+        "drift_gbs": a["drift_bytes"] / (stage_ms["drift"] * 1e-3) / 1e9,
     }
     if with_dense:
         o = torch.empty_like(q)
@@ -248,6 +256,8 @@ def stage_only(tsa, torch, timer, w, x, name, reps):
     comp = [torch.empty(B, H, w.keep, D, dtype=dt, device="cuda") for _ in range(4)]
     tsa.tsa_gather_qkv(desc, q, k, v, idx, comp[0], comp[1], comp[2])
     o = torch.empty_like(q) if name == "dense" else None
+    dws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_DRIFT)), dtype=torch.uint8, device="cuda")
+    dval = torch.empty((), dtype=torch.float64, device="cuda")
     fns = {
         "score": lambda: tsa.tsa_score(desc, q, k, scores, sws),
         "select": lambda: tsa.tsa_select(desc, scores, idx, lws, lws.numel()),
@@ -256,6 +266,7 @@ def stage_only(tsa, torch, timer, w, x, name, reps):
         "scatter": lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r, out, cws),
         "dense": lambda: tsa.tsa_dense_attn(desc, q, k, v, o),
         "forward": lambda: tsa.tsa_forward(desc, q, k, v, r, out, None, None, ws),
+        "drift": lambda: tsa.tsa_drift(desc, r, out, dval, dws),
     }
     ms = timer.run(fns[name], reps)
     return {"workload": w.name, "stage": name, "reps": reps, "avg_ms": ms}

@@ -86,7 +86,7 @@ typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
 typedef enum { TSA_SUBSETS_PER_HEAD = 0, TSA_SUBSETS_PER_KV_HEAD = 1 } tsa_subsets;
 
 /* Which call a workspace is sized for. */
-typedef enum { TSA_OP_SCORE = 0, TSA_OP_SELECT = 1, TSA_OP_SCATTER = 2, TSA_OP_FORWARD = 3 } tsa_op;
+typedef enum { TSA_OP_SCORE = 0, TSA_OP_SELECT = 1, TSA_OP_SCATTER = 2, TSA_OP_FORWARD = 3, TSA_OP_DRIFT = 4 } tsa_op;
 
 typedef struct {
   int32_t B, H, Hkv, L, d;
@@ -191,6 +191,20 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
  * are ignored.  o must not overlap q, k or v. */
 tsa_status tsa_dense_attn(const tsa_desc* desc, const void* q, const void* k, const void* v,
                           void* o, void* stream);
+
+/* Representation drift between a layer's input and output hidden states (skill page,
+ * Step 4, the layer-stability analysis; paper page, Figure 4):
+ *   drift = 1 - (1/T) sum over tokens t of <a_t, b_t> / (max(|a_t|, 1e-12) max(|b_t|, 1e-12)),
+ * over the T = B*L token rows of a, b [B][L][H][d] (dtype; each row is one hidden vector of
+ * H*d values, e.g. the layer's residual input and its output).  Per token the dot product
+ * and the squared norms accumulate in fp32 and the cosine is formed in fp32; the mean
+ * accumulates in fp64 in a fixed order (deterministic).  Out: drift[0], one double in
+ * device memory (8-byte aligned), not written for an empty problem.  Only the sizes and
+ * dtype of desc are used (keep, W, n_sink, subsets, tau are ignored).  Workspace:
+ * TSA_OP_DRIFT (partial sums).  A layer counts as stable once the mean of its last three
+ * drifts is below 0.1 (host logic, not part of the library). */
+tsa_status tsa_drift(const tsa_desc* desc, const void* a, const void* b, double* drift,
+                     void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

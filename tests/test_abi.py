@@ -10,8 +10,8 @@ from tests._lib import ensure_built
 tsa = ensure_built()
 L = tsa.lib()
 
-EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_budget", "tsa_check", "tsa_dense_attn", "tsa_forward",
-            "tsa_gather_qkv",
+EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_budget", "tsa_check", "tsa_dense_attn", "tsa_drift",
+            "tsa_forward", "tsa_gather_qkv",
             "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_status_str", "tsa_workspace_size"]
 
 
@@ -83,6 +83,9 @@ def test_workspace_sizes():
     ad = D(tau=0.01)
     assert tsa.tsa_workspace_size(ad, tsa.TSA_OP_SELECT) >= tsa.tsa_workspace_size(d, tsa.TSA_OP_SELECT) + 32 * 2048 * 8
     assert tsa.tsa_workspace_size(ad, tsa.TSA_OP_FORWARD) > fwd
+    # drift: partial sums only, sized by B*L; the budget fields are not looked at
+    assert 0 < tsa.tsa_workspace_size(D(keep=3), tsa.TSA_OP_DRIFT) <= 2048 * 8
+    assert tsa.tsa_workspace_size(D(L=0, keep=0), tsa.TSA_OP_DRIFT) == 0
 
 
 A = 1 << 40           # fake, well-separated, 16-byte aligned addresses
@@ -141,6 +144,14 @@ def test_entry_points_reject_before_launch():
     assert call("tsa_select", kvd, sc, idx, None, 0, None) == 6
     assert call("tsa_select", kvd, sc, idx, ws, 8 * 8192 * 4, None) == 6
     assert call("tsa_select", kvd, sc, idx, sc + 4096, big, None) == 7
+    # drift
+    assert call("tsa_drift", bd, q, None, o, ws, big, None) == 1
+    assert call("tsa_drift", bd, q, r, o, None, 0, None) == 6
+    assert call("tsa_drift", bd, q, r, o + 4, ws, big, None) == 5
+    assert call("tsa_drift", bd, q, r, q + 64, ws, big, None) == 7
+    assert call("tsa_drift", bd, q, r, o, r + 4096, big, None) == 7
+    assert call("tsa_drift", ctypes.byref(D(keep=2)), q, r, o, ws, 16, None) == 6   # budget not checked
+    assert call("tsa_drift", ctypes.byref(D(d=96)), q, r, o, ws, big, None) == 2
     # descriptor errors come first
     bad = ctypes.byref(D(keep=2))
     assert call("tsa_forward", bad, q, k, v, r, o, None, None, ws, big, None) == 3

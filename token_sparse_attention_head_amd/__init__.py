@@ -28,7 +28,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tsa.h")
 
 TSA_OK = 0
 TSA_F32, TSA_BF16 = 0, 1
-TSA_OP_SCORE, TSA_OP_SELECT, TSA_OP_SCATTER, TSA_OP_FORWARD = 0, 1, 2, 3
+TSA_OP_SCORE, TSA_OP_SELECT, TSA_OP_SCATTER, TSA_OP_FORWARD, TSA_OP_DRIFT = 0, 1, 2, 3, 4
 TSA_SUBSETS_PER_HEAD, TSA_SUBSETS_PER_KV_HEAD = 0, 1
 ABI_VERSION = 3   # TSA_ABI_VERSION of include/tsa.h that this binding's TsaDesc matches
 STATUS_NAMES = {0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_SHAPE", 3: "TSA_ERR_BUDGET", 4: "TSA_ERR_DTYPE",
@@ -68,6 +68,7 @@ _SIGS = {
     "tsa_scatter_residual": ([_DP, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_forward": ([_DP, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_dense_attn": ([_DP, _P, _P, _P, _P, _P], ctypes.c_int),
+    "tsa_drift": ([_DP, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
 }
 
 
@@ -174,6 +175,11 @@ def tsa_forward(desc, q, k, v, residual, out, scores=None, idx=None, ws=None, ws
 
 def tsa_dense_attn(desc, q, k, v, o, stream=None):
     _call("tsa_dense_attn", ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream))
+
+
+def tsa_drift(desc, a, b, out, ws, ws_bytes=None, stream=None):
+    _call("tsa_drift", ctypes.byref(desc), _ptr(a), _ptr(b), _ptr(out), _ptr(ws),
+          ws.numel() if ws_bytes is None else ws_bytes, _stream(stream))
 
 
 # ---- allocating helpers ---------------------------------------------------------------
@@ -308,3 +314,39 @@ def dense_attn(q, k, v, scale=0.0):
     o = torch.empty_like(q)
     tsa_dense_attn(desc, q, k, v, o)
     return o
+
+
+def drift(h_before, h_after):
+    """Representation drift (a 0-dim float64 GPU tensor) of hidden states [B, L, D] or
+    [B, L, H, d] (D = H * d a multiple of 64): 1 - mean over tokens of the cosine of the
+    normalised before/after vectors."""
+    if h_before.shape != h_after.shape or h_before.dtype != h_after.dtype:
+        raise ValueError("hidden states must have the same shape and dtype")
+    for t in (h_before, h_after):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.float32, torch.bfloat16) or t.dim() < 3:
+            raise ValueError("hidden states must be contiguous float32/bfloat16 GPU tensors [B, L, ...]")
+    B, L = h_before.shape[0], h_before.shape[1]
+    D = h_before[0, 0].numel()
+    d = 128 if D % 128 == 0 else 64
+    if D % d:
+        raise ValueError("the hidden size must be a multiple of 64")
+    desc = make_desc(B, D // d, D // d, L, d, 0, 1, 0, h_before.dtype)
+    out = torch.empty((), dtype=torch.float64, device=h_before.device)
+    ws = _workspace(desc, TSA_OP_DRIFT, h_before.device)
+    tsa_drift(desc, h_before, h_after, out, ws)
+    return out
+
+
+class LayerStability:
+    """Host-side stability rule over per-layer drifts: a layer is stable once the mean of
+    the last ``window`` drifts (its own included) is below ``threshold``."""
+
+    def __init__(self, window: int = 3, threshold: float = 0.1):
+        self.window, self.threshold, self.history = window, threshold, []
+
+    def update(self, drift_value: float) -> bool:
+        self.history.append(float(drift_value))
+        if len(self.history) < self.window:
+            return False
+        recent = self.history[-self.window:]
+        return sum(recent) / len(recent) < self.threshold

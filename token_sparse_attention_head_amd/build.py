@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtsa.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "move.hip", "attn.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "move.hip", "attn.hip", "drift.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

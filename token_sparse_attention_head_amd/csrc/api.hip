@@ -180,6 +180,11 @@ tsa_status tsa_check(const tsa_desc* desc) { return check_full(desc); }
 
 tsa_status tsa_workspace_size(const tsa_desc* desc, int op, size_t* bytes) {
   if (!bytes) return TSA_ERR_NULL;
+  if (op == TSA_OP_DRIFT) {   // uses the sizes only
+    TSA_TRY(check_shape(desc));
+    *bytes = round_up(tsa::drift_workspace_bytes(*desc));
+    return TSA_OK;
+  }
   TSA_TRY(check_full(desc));
   const Sizes z = sizes_of(*desc);
   switch (op) {
@@ -360,6 +365,24 @@ tsa_status tsa_dense_attn(const tsa_desc* desc, const void* q, const void* k, co
   if (overlap(ro, {q, z.q}) || overlap(ro, {k, z.kv}) || overlap(ro, {v, z.kv})) return TSA_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(tsa::launch_attn_dense(d, q, k, v, o, s), s);
+}
+
+tsa_status tsa_drift(const tsa_desc* desc, const void* a, const void* b, double* drift, void* ws, size_t ws_bytes,
+                     void* stream) {
+  TSA_TRY(check_shape(desc));
+  const tsa_desc& d = *desc;
+  if (empty_problem(d)) return TSA_OK;
+  if (!a || !b || !drift) return TSA_ERR_NULL;
+  if (!aligned(a) || !aligned(b) || !aligned(ws) || reinterpret_cast<uintptr_t>(drift) % 8 != 0) return TSA_ERR_ALIGN;
+  const Sizes z = sizes_of(d);
+  const size_t need = round_up(tsa::drift_workspace_bytes(d));
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  const Range rw{ws, need}, rd{drift, sizeof(double)};
+  if (overlap(rw, {a, z.q}) || overlap(rw, {b, z.q}) || overlap(rd, {a, z.q}) || overlap(rd, {b, z.q}) ||
+      overlap(rd, rw))
+    return TSA_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(tsa::launch_drift(d, a, b, drift, static_cast<double*>(ws), s), s);
 }
 
 }  // extern "C"

@@ -27,6 +27,11 @@ struct SelectLayout {
   int S, seg;
 };
 SelectLayout select_layout(const tsa_desc& d);
+// Representation drift of [B][L][H*d] hidden states: partial sums in a workspace of
+// drift_workspace_bytes(d) bytes, the result as one double.
+size_t drift_workspace_bytes(const tsa_desc& d);
+hipError_t launch_drift(const tsa_desc& d, const void* a, const void* b, double* out, double* partial,
+                        hipStream_t s);
 // Row budgets [B][R]: keep for every row, or the token-coverage budget when tau > 0.
 hipError_t launch_budget(const tsa_desc& d, const float* scores, int32_t* counts, void* ws, hipStream_t s);
 // Subsets into idx (rows padded with -1 below keep when tau > 0) and optionally the inverse
