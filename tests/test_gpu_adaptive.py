@@ -179,3 +179,18 @@ def test_fused_adaptive_equals_staged(per_kv_head):
     oh = tsa.attn(*tsa.gather_qkv(q, k, v, ig))
     staged = tsa.scatter_residual(oh, ig, r)
     assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+
+
+def test_fused_adaptive_many_heads_without_plan():
+    # More than 4096 (batch, head) pairs: the fused attention takes the interleaved tile
+    # order instead of the per-XCD plan; it still equals the staged path bit for bit.
+    B, H, Hkv, L, d, keep, W, ns, tau = 130, 32, 8, 200, 64, 200, 16, 4, 0.3
+    x = workloads.small_random(B, H, Hkv, L, d, seed=5, dtype="bf16", q_grade=4.0)
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    out, sg, ig = tsa.forward(q, k, v, r, keep, W, ns, return_scores=True, tau=tau)
+    ks = (ig >= 0).sum(dim=-1)
+    assert B * H > 4096 and int(ks.min()) < int(ks.max())
+    assert np.array_equal(ig.cpu().numpy(), oracle.select(sg.cpu().numpy(), keep, W, ns, tau=tau))
+    oh = tsa.attn(*tsa.gather_qkv(q, k, v, ig))
+    staged = tsa.scatter_residual(oh, ig, r)
+    assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
