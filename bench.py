@@ -58,6 +58,7 @@ class Timer:
         self.torch = torch
 
     def run(self, fn, reps):
+        """Mean ms of `reps` back-to-back calls (one pair of events around them all)."""
         t = self.torch
         s = t.cuda.current_stream()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
@@ -68,6 +69,29 @@ class Timer:
         b.record(s)
         t.cuda.synchronize()
         return a.elapsed_time(b) / reps
+
+    def each(self, fn, reps, flush=None):
+        """ms of every call timed alone (events around each call); `flush` runs untimed
+        before each call (cold runs)."""
+        t = self.torch
+        s = t.cuda.current_stream()
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        t.cuda.synchronize()
+        for a, b in ev:
+            if flush is not None:
+                flush()
+            a.record(s)
+            fn()
+            b.record(s)
+        t.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+
+def stats(ms):
+    ms = sorted(ms)
+    n = len(ms)
+    med = ms[n // 2] if n % 2 else 0.5 * (ms[n // 2 - 1] + ms[n // 2])
+    return {"median": med, "min": ms[0], "max": ms[-1], "n": n}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_L128k_r0.5_hbm_traffic.txt")
@@ -131,6 +155,7 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     t0 = time.perf_counter()
     ms_events = timer.run(step, steps)
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_stats = stats(timer.each(step, steps))      # the same steps timed one by one
 
     # Stage by stage through the standalone entry points, same sizes and buffers.
     scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
@@ -150,11 +175,23 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     for name, fn in stages.items():
         fn()
         stage_ms[name] = timer.run(fn, reps)
+    # Each stage timed call by call (median, min), and the HBM-bound stages also cold: a
+    # 1 GiB buffer is written before every call so the 256 MB Infinity Cache holds none of
+    # the stage's inputs.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: scratch.fill_(1)   # noqa: E731
+    stage_stats = {name: {"warm": stats(timer.each(fn, max(reps, 5)))} for name, fn in stages.items()}
+    for name in ("gather", "scatter"):
+        stage_stats[name]["cold"] = stats(timer.each(stages[name], max(reps, 5), flush))
     # Representation drift across the layer (residual in, out): a bandwidth-bound reduction.
     dws = torch.empty(max(1, tsa.tsa_workspace_size(desc, tsa.TSA_OP_DRIFT)), dtype=torch.uint8, device="cuda")
     dval = torch.empty((), dtype=torch.float64, device="cuda")
-    tsa.tsa_drift(desc, r, out, dval, dws)
-    stage_ms["drift"] = timer.run(lambda: tsa.tsa_drift(desc, r, out, dval, dws), reps)
+    drift = lambda: tsa.tsa_drift(desc, r, out, dval, dws)   # noqa: E731
+    drift()
+    stage_ms["drift"] = timer.run(drift, reps)
+    stage_stats["drift"] = {"warm": stats(timer.each(drift, max(reps, 5))),
+                            "cold": stats(timer.each(drift, max(reps, 5), flush))}
+    del scratch
     # In-place scatter variant (out == residual touches only kept rows); on a copy.
     r2 = r.clone()
     stage_ms["scatter_inplace"] = timer.run(lambda: tsa.tsa_scatter_residual(desc, comp[3], idx, r2, r2), reps)
@@ -162,7 +199,9 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
 
     res = {"workload": w.name, "subsets": "per_kv_head" if per_kv_head else "per_head", "keep": w.keep,
            "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events,
-           "wall_ms_per_step": wall_ms, "tokens_per_s": B * L / (ms_events / 1e3), "stage_ms": stage_ms}
+           "wall_ms_per_step": wall_ms, "step_stats_ms": step_stats,
+           "tokens_per_s": B * L / (ms_events / 1e3), "stage_ms": stage_ms,
+           "stage_stats_ms": stage_stats}
     a = algorithmic(w, per_kv_head)
     res["stage_rate"] = {
         "score_tflops": a["score_flops"] / (stage_ms["score"] * 1e-3) / 1e12,
@@ -172,6 +211,9 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
         "scatter_gbs": a["scatter_bytes"] / (stage_ms["scatter"] * 1e-3) / 1e9,
         "drift_gbs": a["drift_bytes"] / (stage_ms["drift"] * 1e-3) / 1e9,
     }
+    res["stage_rate_cold"] = {
+        f"{n}_gbs": a[f"{n}_bytes"] / (stage_stats[n]["cold"]["median"] * 1e-3) / 1e9
+        for n in ("gather", "scatter", "drift")}
     if with_dense:
         o = torch.empty_like(q)
         dense = lambda: tsa.tsa_dense_attn(desc, q, k, v, o)   # noqa: E731
@@ -290,9 +332,12 @@ def cpu_baseline(w, x, budget_s=20.0):
     qb = x["q"][b, :, h, :].astype(np.float64)
     kb = x["k"][b, :, h // G, :].astype(np.float64)
     s = oracle.score_head(qb, kb, w.W, 1.0 / np.sqrt(w.d))
+    t_score = time.perf_counter() - t0
     S = oracle.select_row(s, w.keep, w.W, w.n_sink)
+    t_select = time.perf_counter() - t0 - t_score
     qh, kh, vh = qb[S], kb[S], x["v"][b, S, h // G, :].astype(np.float64)
     t_head = time.perf_counter() - t0
+    t_gather = t_head - t_score - t_select
     # Attention rows: grow the sample until it costs about half the budget.
     n = w.keep
     rows_total = n * (n + 1) / 2.0
@@ -311,11 +356,31 @@ def cpu_baseline(w, x, budget_s=20.0):
     t_scatter = time.perf_counter() - t2
     per_head = t_head + t_scatter + t_att * rows_total / cost
     total = per_head * w.B * w.H
+    heads = w.B * w.H
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()})
+    except Exception:  # pragma: no cover
+        blas = []
     return {"value": w.B * w.L / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{w.name}: head (b=0,h=0) score+select+gather+scatter in full, {len(rows)} of {n} compact "
-                      f"attention rows evenly spaced, scaled by causal row cost and by {w.B * w.H} heads; "
+                      f"attention rows evenly spaced, scaled by causal row cost and by {heads} heads; "
                       f"{t_head + t_att + t_scatter:.1f} s of CPU work",
-            "seconds_per_step_extrapolated": total}
+            "seconds_per_step_extrapolated": total,
+            "seconds_per_stage_extrapolated": {"score": t_score * heads, "select": t_select * heads,
+                                               "gather": t_gather * heads,
+                                               "attention": t_att * rows_total / cost * heads,
+                                               "scatter": t_scatter * heads},
+            "host": {"cpu_model": cpu_model, "affinity_cores": len(os.sched_getaffinity(0)),
+                     "numpy": np.__version__, "blas": blas}}
 
 
 def main():
@@ -400,7 +465,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "L": w.L, "H": w.H, "Hkv": w.Hkv, "d": w.d, "keep": w.keep,
                    "W": w.W, "n_sink": w.n_sink, "parallelism": "single GPU"},
         "speedup_vs_dense": head.get("speedup_vs_dense"), "dense_ms": head.get("dense_ms"),
-        "stage_ms": head["stage_ms"], "stage_rate": head["stage_rate"],
+        "step_stats_ms": head["step_stats_ms"],
+        "stage_ms": head["stage_ms"], "stage_stats_ms": head["stage_stats_ms"], "stage_rate": head["stage_rate"],
+        "stage_rate_cold": head["stage_rate_cold"],
         "sweep": sweep,
         "roofline": roofline, "cpu_baseline": cpu,
     }
