@@ -211,6 +211,16 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
         "scatter_gbs": a["scatter_bytes"] / (stage_ms["scatter"] * 1e-3) / 1e9,
         "drift_gbs": a["drift_bytes"] / (stage_ms["drift"] * 1e-3) / 1e9,
     }
+    peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    res["stage_roofline"] = {
+        name: {"bound": bound, "achieved": res["stage_rate"][key], "peak": peak,
+               "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": res["stage_rate"][key] / peak}
+        for name, key, bound, peak in (("score", "score_tflops", "mfma", peak_mm),
+                                       ("select", "select_gbs", "hbm", PEAK_HBM_GBS),
+                                       ("gather", "gather_gbs", "hbm", PEAK_HBM_GBS),
+                                       ("attn", "attn_tflops", "mfma", peak_mm),
+                                       ("scatter", "scatter_gbs", "hbm", PEAK_HBM_GBS),
+                                       ("drift", "drift_gbs", "hbm", PEAK_HBM_GBS))}
     res["stage_rate_cold"] = {
         f"{n}_gbs": a[f"{n}_bytes"] / (stage_stats[n]["cold"]["median"] * 1e-3) / 1e9
         for n in ("gather", "scatter", "drift")}
@@ -467,7 +477,7 @@ def main():
         "speedup_vs_dense": head.get("speedup_vs_dense"), "dense_ms": head.get("dense_ms"),
         "step_stats_ms": head["step_stats_ms"],
         "stage_ms": head["stage_ms"], "stage_stats_ms": head["stage_stats_ms"], "stage_rate": head["stage_rate"],
-        "stage_rate_cold": head["stage_rate_cold"],
+        "stage_rate_cold": head["stage_rate_cold"], "stage_roofline": head["stage_roofline"],
         "sweep": sweep,
         "roofline": roofline, "cpu_baseline": cpu,
     }
