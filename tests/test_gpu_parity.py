@@ -147,7 +147,12 @@ def test_compact_with_keep_all_equals_dense():
 @pytest.mark.parametrize("dt,d,B,H,Hkv,L,W", [("bf16", 128, 1, 8, 2, 1000, 64), ("bf16", 128, 2, 4, 4, 333, 5),
                                               ("bf16", 64, 1, 4, 1, 2048, 32), ("fp32", 64, 1, 4, 4, 512, 32),
                                               ("fp32", 128, 1, 2, 1, 97, 64), ("bf16", 128, 1, 2, 2, 40, 64),
-                                              ("fp32", 64, 1, 2, 2, 77, 1)])
+                                              ("fp32", 64, 1, 2, 2, 77, 1),
+                                              # bf16 head groups: two quads (G = 8), partial quads (G = 2, 3),
+                                              # d = 64 with 64 window rows, many chunks with a ragged end, L = 1
+                                              ("bf16", 128, 1, 16, 2, 1500, 64), ("bf16", 128, 2, 6, 2, 700, 40),
+                                              ("bf16", 64, 1, 4, 2, 3001, 64), ("bf16", 128, 1, 2, 1, 20000, 64),
+                                              ("bf16", 128, 1, 4, 1, 1, 64)])
 def test_score(dt, d, B, H, Hkv, L, W):
     x = workloads.small_random(B, H, Hkv, L, d, seed=13, dtype=dt)
     s = host(tsa.score(dev(x["q"], dt), dev(x["k"], dt), W))
