@@ -32,6 +32,9 @@
 // * Query tiles are issued longest first; all tiles of a head go to one XCD (workgroup
 //   IDs are dealt to the 8 XCDs round-robin) and an XCD runs one head's tiles before the
 //   next head's, so its concurrent workgroups stream the same K/V tiles through its L2.
+//   With adaptive budgets (rows differ per head) attn_plan_kernel first deals the heads,
+//   sorted by attention work, to the XCDs in snake order, keeping that locality while
+//   the XCDs get equal work.
 #include "common.h"
 #include "kernels.h"
 

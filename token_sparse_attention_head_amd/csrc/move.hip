@@ -10,7 +10,9 @@
 //
 // Every thread moves 16-byte vectors; one row of d elements is 128-512 bytes, so a
 // wave reads and writes whole 128-byte lines.  Kept rows are read once per query head;
-// the out-of-place scatter streams residual and out once in memory order.
+// the out-of-place scatter streams residual and out once in memory order.  An index
+// entry outside [0, L) (the -1 padding of rows below an adaptive budget) moves nothing:
+// gather writes zero rows for it and scatter skips it.
 #include "common.h"
 #include "kernels.h"
 
