@@ -153,16 +153,17 @@ def _end_to_end(x, dt, keep, W, ns, tau, in_place=False, per_kv_head=False, scal
     (1, 8, 2, 1500, 128, 1500, 64, 4, 0.3, True, False),
     (1, 8, 2, 1500, 128, 1500, 64, 4, 0.2, False, True),
     (1, 4, 4, 999, 64, 999, 16, 4, 0.5, False, False),
+    (2, 8, 2, 1100, 128, 900, 64, 4, 0.25, True, True),       # per KV head, in place, B = 2
 ])
 def test_forward_bf16_adaptive(B, H, Hkv, L, d, keep, W, ns, tau, in_place, per_kv_head):
     x = workloads.small_random(B, H, Hkv, L, d, seed=L + 11, dtype="bf16", q_grade=4.0)
     _end_to_end(x, "bf16", keep, W, ns, tau, in_place, per_kv_head)
 
 
-@pytest.mark.parametrize("in_place", [False, True])
-def test_forward_fp32_adaptive(in_place):
+@pytest.mark.parametrize("in_place,per_kv_head", [(False, False), (True, False), (False, True)])
+def test_forward_fp32_adaptive(in_place, per_kv_head):
     x = workloads.small_random(1, 4, 2, 640, 64, seed=9, dtype="fp32", q_grade=3.0)
-    _end_to_end(x, "fp32", 640, 32, 4, 0.25, in_place)
+    _end_to_end(x, "fp32", 640, 32, 4, 0.25, in_place, per_kv_head)
 
 
 @pytest.mark.parametrize("per_kv_head", [False, True])
