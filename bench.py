@@ -137,6 +137,24 @@ def algorithmic(w, per_kv_head=False):
     }
 
 
+def graph_step_ms(torch, timer, step, steps):
+    """ms per step when the whole step is captured once in a HIP graph and replayed (the
+    launches of its kernels then cost no host round trips)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    ms = timer.run(g.replay, steps)
+    del g
+    return ms
+
+
 def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per_kv_head=False):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
@@ -156,6 +174,7 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     ms_events = timer.run(step, steps)
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_stats = stats(timer.each(step, steps))      # the same steps timed one by one
+    graph_ms = graph_step_ms(torch, timer, step, steps)
 
     # Stage by stage through the standalone entry points, same sizes and buffers.
     scores = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
@@ -200,6 +219,7 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
     res = {"workload": w.name, "subsets": "per_kv_head" if per_kv_head else "per_head", "keep": w.keep,
            "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events,
            "wall_ms_per_step": wall_ms, "step_stats_ms": step_stats,
+           "graph_ms_per_step": graph_ms, "graph_tokens_per_s": B * L / (graph_ms / 1e3),
            "tokens_per_s": B * L / (ms_events / 1e3), "stage_ms": stage_ms,
            "stage_stats_ms": stage_stats}
     a = algorithmic(w, per_kv_head)
@@ -232,6 +252,7 @@ def gpu_case(tsa, torch, timer, w, x, args, reps, steps, warmup, with_dense, per
         res["dense_ms"] = dms
         res["dense_tflops"] = a["dense_flops"] / (dms * 1e-3) / 1e12
         res["speedup_vs_dense"] = dms / ms_events
+        res["graph_speedup_vs_dense"] = dms / graph_ms
         res["attn_speedup_vs_dense"] = dms / stage_ms["attn"]
         del o
     del ws, comp, out
@@ -432,6 +453,7 @@ def main():
             if "dense_ms" in head:
                 res["dense_ms"] = head["dense_ms"]
                 res["speedup_vs_dense"] = head["dense_ms"] / res["ms_per_step"]
+                res["graph_speedup_vs_dense"] = head["dense_ms"] / res["graph_ms_per_step"]
                 res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
             log(f"{wi.name}: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
             sweep.append(res)
@@ -443,6 +465,7 @@ def main():
             if "dense_ms" in head:
                 res["dense_ms"] = head["dense_ms"]
                 res["speedup_vs_dense"] = head["dense_ms"] / res["ms_per_step"]
+                res["graph_speedup_vs_dense"] = head["dense_ms"] / res["graph_ms_per_step"]
                 res["attn_speedup_vs_dense"] = head["dense_ms"] / res["stage_ms"]["attn"]
             log(f"{wi.name} per KV head: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
             sweep.append(res)
@@ -476,6 +499,7 @@ def main():
                    "W": w.W, "n_sink": w.n_sink, "parallelism": "single GPU"},
         "speedup_vs_dense": head.get("speedup_vs_dense"), "dense_ms": head.get("dense_ms"),
         "step_stats_ms": head["step_stats_ms"],
+        "graph_ms_per_step": head["graph_ms_per_step"], "graph_tokens_per_s": head["graph_tokens_per_s"],
         "stage_ms": head["stage_ms"], "stage_stats_ms": head["stage_stats_ms"], "stage_rate": head["stage_rate"],
         "stage_rate_cold": head["stage_rate_cold"], "stage_roofline": head["stage_roofline"],
         "sweep": sweep,
