@@ -23,6 +23,8 @@
 // reads its MFMA operands from there, so the K bytes cross HBM once and enough of them are
 // in flight to hide its latency.  fp32: every wave reads its operands straight from global
 // memory (a lane reads one contiguous half of a head-dim row).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -324,26 +326,31 @@ __global__ __launch_bounds__(256) void score_pass1_lds_kernel(const __bf16* __re
       __builtin_amdgcn_sched_barrier(0);
       HalfRow<__bf16, D> kf;
       lds_key<D>(tile, kb, lane, kf);
-      const bool need_mask = j0 + 31 > first_row_pos;
+      // The causal mask only touches the blocks that reach the window rows: those take a
+      // separate copy of the code so the others run without per-element selects.
+      auto rows = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x16 acc = {};
-        acc = dot_tile<__bf16, D>(acc, kf, qf[rb]);   // rows: keys, columns: window queries
-        const int i = first_row_pos + rb * 32 + (lane & 31);
-        float tmax = -__builtin_huge_valf();
+        for (int rb = 0; rb < RB; ++rb) {
+          f32x16 acc = {};
+          acc = dot_tile<__bf16, D>(acc, kf, qf[rb]);   // rows: keys, columns: window queries
+          const int i = first_row_pos + rb * 32 + (lane & 31);
+          float tmax = -__builtin_huge_valf();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + acc_row(r, hf);
-          if (need_mask && j > i) acc[r] = -__builtin_huge_valf();
-          tmax = fmaxf(tmax, acc[r]);
+          for (int r = 0; r < 16; ++r) {
+            if (MASK && j0 + acc_row(r, hf) > i) acc[r] = -__builtin_huge_valf();
+            tmax = fmaxf(tmax, acc[r]);
+          }
+          const float mn = fmaxf(m[rb], tmax * c);
+          float add = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mn));
+          sacc[rb] = sacc[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + add;
+          m[rb] = mn;
         }
-        const float mn = fmaxf(m[rb], tmax * c);
-        float add = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mn));
-        sacc[rb] = sacc[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + add;
-        m[rb] = mn;
-      }
+      };
+      if (j0 + 31 > first_row_pos) rows(std::true_type{});
+      else rows(std::false_type{});
     }
   };
   for (int t = 0; t < nt; t += 2) {
@@ -417,20 +424,23 @@ __global__ __launch_bounds__(256, 2) void score_pass2_lds_kernel(const __bf16* _
       HalfRow<__bf16, D> kf;
       lds_key<D>(tile, kb, lane, kf);
       const int j = j0 + (lane & 31);
-      const bool need_mask = j0 + 31 > first_row_pos;
-      float col = 0.f;
+      auto cols = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float col = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x16 acc = {};
-        acc = dot_tile<__bf16, D>(acc, qf[rb], kf);   // rows: window queries, columns: keys
+        for (int rb = 0; rb < RB; ++rb) {
+          f32x16 acc = {};
+          acc = dot_tile<__bf16, D>(acc, qf[rb], kf);   // rows: window queries, columns: keys
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = first_row_pos + rb * 32 + acc_row(r, hf);
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mrow[rb][r])) * il[rb][r];
-          if (need_mask && j > i) p = 0.f;
-          col += p;
+          for (int r = 0; r < 16; ++r) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mrow[rb][r])) * il[rb][r];
+            if (MASK && j > first_row_pos + rb * 32 + acc_row(r, hf)) p = 0.f;
+            col += p;
+          }
         }
-      }
+        return col;
+      };
+      float col = j0 + 31 > first_row_pos ? cols(std::true_type{}) : cols(std::false_type{});
       col += xor32(col);
       if (hf == 0 && j < j_end) out[j] = col;
     }
