@@ -108,7 +108,9 @@ const char* tsa_status_str(int status);
 
 /* Host-only validation of a descriptor (no HIP call).  Forced set
  * F = [0, min(n_sink, L)) U [L - min(W, L), L); keep must satisfy |F| <= keep <= L;
- * subsets must be a tsa_subsets value (else TSA_ERR_ARG). */
+ * subsets must be a tsa_subsets value (else TSA_ERR_ARG).  Index limits (else
+ * TSA_ERR_SHAPE): B * H <= 65535, L * H * d * e < 2^35 and one batch entry's K (and V),
+ * L * Hkv * d * e bytes, below 4 GiB (e = bytes per element). */
 tsa_status tsa_check(const tsa_desc* desc);
 
 /* Host-only: bytes of workspace the call `op` needs for `desc` (written to *bytes). */

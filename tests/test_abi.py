@@ -46,6 +46,10 @@ def test_header_declares_and_library_exports_every_entry_point():
     (dict(L=0, keep=0), 0),                    # empty problem: nothing to do
     (dict(B=0), 0),
     (dict(B=4096, H=32), 2),                   # grid limit
+    # one batch entry's K below 4 GiB: L * Hkv * d * 2 < 2^32 (H = Hkv = 8, d = 128 bf16)
+    (dict(H=8, Hkv=8, L=(1 << 21) - 64, keep=4096), 0),
+    (dict(H=8, Hkv=8, L=1 << 21, keep=4096), 2),
+    (dict(H=8, Hkv=8, L=1 << 20, keep=4096, dtype=0), 2),   # fp32: 4 bytes per element
     (dict(subsets=1), 0),                      # one subset per KV head
     (dict(subsets=2), 9), (dict(subsets=-1), 9),
     (dict(tau=0.005), 0), (dict(tau=1.0), 0),  # adaptive budgets

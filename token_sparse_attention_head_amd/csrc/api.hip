@@ -45,6 +45,8 @@ tsa_status check_shape(const tsa_desc* d) {
   if ((int64_t)d->B * d->H > 65535) return TSA_ERR_SHAPE;
   const int64_t chunks_per_row = (int64_t)d->d * elem_bytes(*d) / 16;
   if ((int64_t)d->L * d->H * chunks_per_row >= (int64_t)1 << 31) return TSA_ERR_SHAPE;
+  // The attention kernels address K and V rows by 32-bit byte offsets within one batch entry.
+  if ((int64_t)d->L * d->Hkv * d->d * elem_bytes(*d) >= (int64_t)1 << 32) return TSA_ERR_SHAPE;
   return TSA_OK;
 }
 

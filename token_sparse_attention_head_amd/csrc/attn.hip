@@ -11,24 +11,29 @@
 //   o_t = sum_{u <= t} softmax_u(scale <q_t, k_u>) v_u,   fp32 accumulation, one rounding.
 //
 // Design for gfx950 (CDNA4):
-// * A workgroup is NW waves over BM = NW * QB * 32 query rows of one (batch, head); each
-//   wave keeps its QB blocks of 32 query rows in registers as MFMA operands.  The bf16
-//   kernel runs 8 waves (2 per SIMD) within 256 registers each, so one wave's softmax
-//   arithmetic issues while the other wave's matrix instructions run.
-// * Key/value tiles of 64 rows stream through LDS, double buffered; the global loads of
-//   the next two tiles are in flight in registers while the current tile is on the
-//   matrix cores.
-// * Scores are formed transposed, S^T = K Q^T (32x32x16 bf16 MFMA), so a lane owns one
-//   query and 16 keys per 32-key block and the row sums stay lane-local.
+// * bf16: a workgroup is 8 waves (2 per SIMD, within 256 registers each, so one wave's
+//   softmax arithmetic issues while the other wave's matrix instructions run) over 384
+//   query rows of one (batch, head).  Each wave keeps 48 query rows in registers as the
+//   operands of three 16-row blocks on the 16x16x32 bf16 MFMA, so each K or V operand it
+//   reads from LDS feeds three blocks: LDS operand traffic, the kernel's main cost, per
+//   unit of matrix work is two thirds of what 32-row blocks on the 32x32x16 MFMA need.
+//   fp32: 4 waves of 32 query rows on the 32x32x2 fp32 MFMA.
+// * Key/value tiles of 64 rows stream through LDS, double buffered, with the global loads
+//   of the next tile in flight in registers while the current tile is on the matrix
+//   cores.
+// * Scores are formed transposed, S^T = K Q^T, so a lane owns one query of each block and
+//   its row sums stay lane-local (a row's keys are split over four lanes in the bf16
+//   kernel, two in the fp32 one; they are combined once, at the end).
 // * O^T = V^T P^T: the probabilities a lane already holds are the B operand as they
-//   are, and V^T is read from V's natural [key][d] rows with the transposing LDS read
-//   ds_read_b64_tr_b16.  LDS rows are padded (K: 2d + 16 bytes, V: 2d + 64 bytes) so
-//   neither operand read has bank conflicts.
-// * Online softmax in exp2 units against a lazily moved reference: a tile's
-//   probabilities are taken against the current reference without a row max, and the
-//   tile's probability sum tells whether that was safe (below 2^32 nothing is near
-//   overflow).  Only when it is not (the first tile, or a row max that jumped) does the
-//   exact max move the reference and rescale O and l.
+//   are; the bf16 kernel reads V^T from V's natural [key][d] rows with the transposing
+//   LDS read ds_read_b64_tr_b16.  LDS rows are padded so no operand read has bank
+//   conflicts.
+// * Online softmax in exp2 units against a lazily moved reference: a key block's
+//   probabilities (32 keys in the bf16 kernel, a 64-key tile in the fp32 one) are taken
+//   against the current reference without a row max, and their sum tells whether that
+//   was safe (below 2^32 nothing is near overflow).  Only when it is not (the first
+//   block, or a row max that jumped) does the exact max move the reference and rescale
+//   O and l.
 // * Query tiles are issued longest first; all tiles of a head go to one XCD (workgroup
 //   IDs are dealt to the 8 XCDs round-robin) and an XCD runs one head's tiles before the
 //   next head's, so its concurrent workgroups stream the same K/V tiles through its L2.
@@ -376,18 +381,33 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
 
 // ---- bf16 kernel ------------------------------------------------------------------------
 //
-// Same dataflow as attn_kernel, with the gfx950 transposing LDS read for the P.V operand:
-// ds_read_b64_tr_b16 hands lane i of each 16-lane block element i % 4 of the 8 bytes that
-// lanes 4j + i/4 (j = 0..3) address.  Pointing lane s at V[k0 + s/4][d0 + 4 (s%4) .. +3]
-// of a row-major [key][d] tile therefore gives lane i the values V[k0 + j][d0 + i]: the
-// V^T operand, read straight from the natural layout.  K and V tiles are both stored as
-// loaded (one 16-byte store per chunk, no shuffling).  Rows are padded instead of
-// swizzled, so every operand address is one register plus an immediate: K rows are
-// 2d+16 bytes apart (consecutive keys move 4 banks, so the 16 rows one read cycle touches
-// cover every bank once), V rows 2d+64 apart (a transposing read serves 32 lanes per
-// cycle from 64 banks: four key rows x two 16-lane blocks must fall on disjoint 8-bank
-// ranges, which needs rows 16 banks apart; measured conflict-free, 2d+32 is not).  The tile loop is unrolled by two so the buffer offsets are
-// immediates too, and the row pointers of the global loads advance by one add per tile.
+// 48 query rows per wave as three 16-row blocks on v_mfma_f32_16x16x32_bf16.  16x16 output
+// tiles: lane l holds column (l % 16) and rows 4*(l/16) + i, i = 0..3; operand A: lane l
+// supplies row (l % 16) and the contraction slice 8*(l/16) .. +7; operand B: column
+// (l % 16) and the same slice.  Every K and V operand a wave reads from LDS feeds its three
+// query blocks, so a 64-key tile's LDS operand bytes serve 48 query rows per wave.
+//
+// Scores: S^T (16 keys x 16 queries) = K Q^T.  Lane group g = l/16 covers the contiguous
+// quarter d in [g*D/4, (g+1)*D/4) of the contraction (K and Q use the same split, which
+// leaves every dot product unchanged), so a lane's Q operands are its query row's quarter
+// and its K operands 16-byte reads of one key row.  The lane then owns query (l % 16) of
+// each block and keys 4g .. 4g+3 of each 16-key block.
+//
+// P.V: O^T (16 d x 16 queries) += V^T (16 d x 32 keys) P^T.  A lane's P^T operand is its
+// own 8 probabilities of the 32-key half, keys {4g .. 4g+3} and {16+4g .. 16+4g+3}; the V^T
+// operand must cover the same keys, which the transposing LDS read ds_read_b64_tr_b16
+// gives from V's natural [key][d] rows: it hands lane i of each 16-lane block element
+// i % 4 of the 8 bytes that lanes 4j + i/4 (j = 0..3) address, so pointing lane s at
+// V[k0 + s/4][d0 + 4 (s%4) .. +3] gives lane i the values V[k0 + j][d0 + i].  Two such
+// reads (k0 = 4g and 16 + 4g) make the operand.
+//
+// LDS rows are padded, not swizzled, so every operand address is one register plus an
+// immediate.  K rows are 2d+16 bytes apart: the 16 lanes of one 16-byte read cycle read
+// 16 consecutive key rows at one column, 4 banks apart.  V rows are 2d+32 bytes apart: one
+// transposing read cycle serves 32 lanes, eight key rows of 8 banks each, and rows 2d+32
+// bytes apart land 8 banks apart (2d+64, the pitch for a 32x32 operand layout, puts rows
+// four apart on the same banks).  The tile loop is unrolled by two so the buffer offsets
+// are immediates too.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -400,12 +420,12 @@ __device__ __forceinline__ bf16x8 tr_read2(const char* a, const char* b) {
   return __builtin_bit_cast(bf16x8, z);
 }
 
-// Value of the other 32-lane half (lane l ^ 32) in one VALU instruction: v_permlane32_swap
-// of a register pair returns {lo, lo} and {hi, hi}.
-__device__ __forceinline__ float half_swap(float x) {
-  const u32x2 pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(__lane_id() < 32 ? pr[1] : pr[0]);
+__device__ __forceinline__ f32x4 mfma16(f32x4 c, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+constexpr int BF16_QB = 3;                 // 16-row query blocks per wave
+constexpr int BF16_WQ = 16 * BF16_QB;      // query rows per wave
 
 // MODE selects where rows live: ATT_COMPACT (contiguous [B][H][n][d] compact tensors),
 // ATT_DENSE ([B][L][H][d] and [B][L][Hkv][d], all L rows: the dense reference) or
@@ -413,14 +433,17 @@ __device__ __forceinline__ float half_swap(float x) {
 // [B][L][H][d] / [B][L][Hkv][d], and the epilogue writes residual + O into those rows of
 // the output: the fused forward, which never materialises Q^, K^, V^ or O^).
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) {
-  constexpr bool DENSE = MODE == ATT_DENSE, FUSED = MODE == ATT_FUSED, STRIDED = MODE != ATT_COMPACT;
+__global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams p) {
+  constexpr bool FUSED = MODE == ATT_FUSED, STRIDED = MODE != ATT_COMPACT;
   constexpr int NT = NW * TSA_WAVE;
-  constexpr int BM = NW * 32;
+  constexpr int QB = BF16_QB, WQ = BF16_WQ;
+  constexpr int BM = NW * WQ;
+  constexpr int ST = D / 32;                      // MFMA steps over d
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / NT;            // chunks per lane per tensor per tile
   static_assert(LOADS >= 1 && BN * CPR % NT == 0, "a tile splits evenly over the lanes");
-  constexpr int KP = 2 * D + 16, VP = 2 * D + 64; // padded row pitches, bytes
+  constexpr int RSTEP = NT / CPR;                 // rows between a lane's chunks
+  constexpr int KP = 2 * D + 16, VP = 2 * D + 32; // padded row pitches, bytes
   struct Buf {
     char k[BN * KP];
     char v[BN * VP];
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const int tid = threadIdx.x;
   const int wave = tid / TSA_WAVE;
   const int lane = lane_id();
-  const int hf = lane >> 5, lc = lane & 31;
+  const int g = lane >> 4, lq = lane & 15;
 
   int bh, tile, n = p.n;
   {
@@ -477,39 +500,34 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
   const int h = bh % p.H;
   const int kvh = h / kv_div;
   const __bf16* qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_b + h * p.q_h;
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h;
+  const char* kb8 = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h);
+  const char* vb8 = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h);
   __bf16* obase = reinterpret_cast<__bf16*>(p.o) + b * p.o_b + h * p.o_h;
   const int32_t* idx_bh = FUSED ? p.idx + (b * (p.H / p.idx_div) + h / p.idx_div) * (int64_t)p.n : nullptr;
 
   const int q0 = tile * BM;
-  const int wrow0 = q0 + wave * 32;
-  const int wave_last = min(n - 1, wrow0 + 31);
+  const int wrow0 = q0 + wave * WQ;
+  const int wave_last = min(n - 1, wrow0 + WQ - 1);
   const int nkt = (min(n, q0 + BM) - 1) / BN + 1;
 
-  // Staging: chunk i of this lane is row lrow[i], chunk lchunk[i] of the tile.
-  int lrow[LOADS], lchunk[LOADS], soff_k[LOADS], soff_v[LOADS];
-  const __bf16* kptr[LOADS];
-  const __bf16* vptr[LOADS];
-  int pnext[LOADS];                                  // fused: positions of the next tile's rows
+  // Staging: chunk i of this lane is row lrow + i * RSTEP, 16-byte chunk lch of the tile.
+  // Global offsets are 32-bit bytes from the head's K / V base (the host keeps one batch
+  // entry's K and V below 4 GiB).
+  const int lrow = tid / CPR, lch = tid % CPR;
+  const int soff_k = lrow * KP + lch * 16, soff_v = lrow * VP + lch * 16;
+  const uint32_t rbytes = (uint32_t)(k_r * 2);
+  uint32_t goff = lrow * rbytes + lch * 16;       // chunk 0 of the next tile
+  int pnext[LOADS];                               // fused: positions of the next tile's rows
+  if (FUSED) {
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int e = tid + NT * i;
-    lchunk[i] = e % CPR;
-    lrow[i] = e / CPR;
-    soff_k[i] = lrow[i] * KP + lchunk[i] * 16;
-    soff_v[i] = lrow[i] * VP + lchunk[i] * 16;
-    kptr[i] = kbase + (int64_t)lrow[i] * k_r + lchunk[i] * 8;
-    vptr[i] = vbase + (int64_t)lrow[i] * k_r + lchunk[i] * 8;
-    if (FUSED) pnext[i] = idx_bh[min(lrow[i], n - 1)];
+    for (int i = 0; i < LOADS; ++i) pnext[i] = idx_bh[min(lrow + i * RSTEP, n - 1)];
   }
-  constexpr int PF = 2;                              // tiles in flight in registers
-  u32x4 kst[PF][LOADS], vst[PF][LOADS];
+  u32x4 kst[LOADS], vst[LOADS];                   // the next tile, in flight in registers
   int next_k0 = 0;
   // Loads the next tile into registers; rows past the end repeat the last row (they
   // only meet queries that mask them).  Fused: the rows' positions were fetched one tile
   // earlier, and this fetches the positions of the tile after.
-  auto load_next = [&](int set) __attribute__((always_inline)) {
+  auto load_next = [&]() __attribute__((always_inline)) {
     if (FUSED) {
       // The next tile's positions are requested before this tile's rows: loads complete
       // in order, so waiting for the positions later does not wait for the rows.
@@ -517,198 +535,206 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_bf16_kernel(AttnParams p) 
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         pcur[i] = pnext[i];
-        pnext[i] = idx_bh[min(next_k0 + BN + lrow[i], n - 1)];
+        pnext[i] = idx_bh[min(next_k0 + BN + lrow + i * RSTEP, n - 1)];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int64_t off = (int64_t)pcur[i] * k_r + lchunk[i] * 8;
-        kst[set][i] = ld16(kbase + off);
-        vst[set][i] = ld16(vbase + off);
+        const uint32_t off = (uint32_t)pcur[i] * rbytes + lch * 16;
+        kst[i] = ld16(kb8 + off);
+        vst[i] = ld16(vb8 + off);
       }
-      next_k0 += BN;
-      return;
-    }
-    if (next_k0 + BN <= n) {
+    } else if (next_k0 + BN <= n) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        kst[set][i] = ld16(kptr[i]);
-        vst[set][i] = ld16(vptr[i]);
+        kst[i] = ld16(kb8 + (goff + i * RSTEP * rbytes));
+        vst[i] = ld16(vb8 + (goff + i * RSTEP * rbytes));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int64_t back = (int64_t)(max(next_k0 + lrow[i] - (n - 1), 0)) * k_r;
-        kst[set][i] = ld16(kptr[i] - back);
-        vst[set][i] = ld16(vptr[i] - back);
+        const uint32_t off = (uint32_t)min(next_k0 + lrow + i * RSTEP, n - 1) * rbytes + lch * 16;
+        kst[i] = ld16(kb8 + off);
+        vst[i] = ld16(vb8 + off);
       }
     }
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      kptr[i] += BN * k_r;
-      vptr[i] += BN * k_r;
-    }
+    goff += BN * rbytes;
     next_k0 += BN;
   };
 
-  HalfRow<__bf16, D> qf;
-  {
-    const int row = wrow0 + lc;
-    if (row < n)
-      qf.load(qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + hf * (D / 2));
-    else
-      qf.zero();
+  // Q operands: block qb, step s = 8 values of row wrow0 + 16 qb + lq from d = g*D/4 + 8 s.
+  bf16x8 qf[QB][ST];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 16 * qb + lq;
+    if (row < n) {
+      const __bf16* src = qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + g * (D / 4);
+#pragma unroll
+      for (int s = 0; s < ST; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8*>(src + 8 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < ST; ++s) qf[qb][s] = bf16x8{};
+    }
   }
-  const int koff = lc * KP + hf * D;                   // QK operand: key lc, d from hf * D/2
-  const int blk = lane >> 4, sl = lane & 15;
-  const int voff = (4 * (blk >> 1) + (sl >> 2)) * VP + (16 * (blk & 1) + 4 * (sl & 3)) * 2;
+  const int koff = lq * KP + g * (D / 4) * 2;                      // K operand: key lq, quarter g
+  const int voff = (4 * g + (lq >> 2)) * VP + 4 * (lq & 3) * 2;   // V^T operand, see above
 
-  f32x16 o[D / 32];
-  float m = NEG_BIG, l = 0.f;
+  f32x4 o[D / 16][QB];
+  float m[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = NEG_BIG;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db][qb] = f32x4{};
+  }
 
-  // O^T += V^T P^T for one tile.
-  auto pv = [&](const Buf& buf, const bf16x8 (&pf)[KB][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const char* a = buf.v + (kb * 32 + 16 * jj) * VP + voff + db * 64;
-          o[db] = mfma(o[db], tr_read2(a, a + 8 * VP), pf[kb][jj]);
-        }
-  };
-  auto step = [&](int t, Buf& cur, int set) __attribute__((always_inline)) {
+  auto step = [&](int t, Buf& cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      *reinterpret_cast<u32x4*>(cur.k + soff_k[i]) = kst[set][i];
-      *reinterpret_cast<u32x4*>(cur.v + soff_v[i]) = vst[set][i];
+      *reinterpret_cast<u32x4*>(cur.k + soff_k + i * RSTEP * KP) = kst[i];
+      *reinterpret_cast<u32x4*>(cur.v + soff_v + i * RSTEP * VP) = vst[i];
     }
     __syncthreads();
     // Unconditional (past the end it re-reads the clamped last rows): every step then
     // issues the same loads, so the wait before a store only waits for that tile.
-    load_next(set);
+    load_next();
     const int k0 = t * BN;
     if (wrow0 > wave_last || k0 > wave_last) return;   // no key of this tile is visible
-
-    f32x16 s[KB];
-    // Each 32-key block's eight K operands are read before its MFMAs so the reads
-    // overlap one another instead of each MFMA waiting for its own.
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8 kf[D / 16];
+    for (int hh = 0; hh < BN / 32; ++hh) {
+      const int kh = k0 + 32 * hh;
+      if (kh > wave_last) break;
+      // S^T blocks: keys kh + 16 kk + 4 g + i, query 16 qb + lq.  Each 16-key block's K
+      // operands are read before its MFMAs so the reads overlap one another.
+      f32x4 s[2][QB];
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) kf[s2] = *reinterpret_cast<const bf16x8*>(cur.k + kb * 32 * KP + koff + s2 * 16);
-      __builtin_amdgcn_sched_barrier(0);
-      s[kb] = f32x16{};
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 kf[ST];
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) s[kb] = mfma(s[kb], kf[s2], qf.f[s2]);
-    }
-
-    // Online softmax of the tile (mask only where the tile reaches the diagonal).
-    // Probabilities against the running reference m; the tile's probability sum
-    // guards it (below 2^32 nothing is near overflow), else the exact max rescales.
-    const bool diag = k0 + BN - 1 > wrow0;
-    if (diag) {
-      const int lim = wrow0 + lc - k0 - 4 * hf;
+        for (int st = 0; st < ST; ++st)
+          kf[st] = *reinterpret_cast<const bf16x8*>(cur.k + (32 * hh + 16 * kk) * KP + koff + st * 16);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int qb = 0; qb < QB; ++qb) s[kk][qb] = f32x4{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_row(r, 0) > lim - 32 * kb) s[kb][r] = -__builtin_huge_valf();
-    }
-    bf16x8 pf[KB][2];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-    auto probs = [&](float mref) __attribute__((always_inline)) {
+        for (int st = 0; st < ST; ++st)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+          for (int qb = 0; qb < QB; ++qb) s[kk][qb] = mfma16(s[kk][qb], kf[st], qf[qb][st]);
+      }
+      if (kh + 31 > wrow0) {                       // the half reaches the diagonal
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mref));
-          ls[r & 3] += pr;
-          pf[kb][r >> 3][r & 7] = static_cast<__bf16>(pr);
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kh + 16 * kk + 4 * g + i > wrow0 + 16 * qb + lq) s[kk][qb][i] = -__builtin_huge_valf();
+      }
+      // Online softmax of the half: probabilities against the running reference m; the
+      // probability sums guard it (below 2^32 nothing is near overflow), else the exact
+      // row max (over the four lane groups) moves m and rescales O and l.
+      bf16x8 pf[QB];
+      float ls[QB];
+      auto probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][qb][i], c, -m[qb]));
+              if (i & 1) a1 += pr; else a0 += pr;
+              pf[qb][4 * kk + i] = static_cast<__bf16>(pr);
+            }
+          ls[qb] = a0 + a1;
         }
-    };
-    probs(m);
-    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    if (__ballot(!(lsum < 4294967296.0f)) != 0) {
-      float tmax = -__builtin_huge_valf();
+      };
+      probs();
+      bool unsafe = false;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) unsafe |= !(ls[qb] < 4294967296.0f);
+      if (__ballot(unsafe) != 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-      tmax = fmaxf(tmax, half_swap(tmax));
-      const float mn = fmaxf(m, tmax * c);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
+        for (int qb = 0; qb < QB; ++qb) {
+          float tmax = -__builtin_huge_valf();
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-      m = mn;
-      ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
-      probs(mn);
-      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kk][qb][i]);
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16, TSA_WAVE));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, TSA_WAVE));
+          const float mn = fmaxf(m[qb], tmax * c);
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
+          m[qb] = mn;
+        }
+        probs();
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const char* a = cur.v + (32 * hh) * VP + voff + db * 32;
+        const bf16x8 va = tr_read2(a, a + 16 * VP);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma16(o[db][qb], va, pf[qb]);
+      }
     }
-    l += lsum;
-    pv(cur, pf);
   };
 
-  load_next(0);
-  if (PF == 2) load_next(PF - 1);
+  load_next();
   // Steps run in pairs; a step past the last tile only stages and meets the barrier
   // (no wave sees its keys), which keeps the loop body free of conditions.
   for (int t = 0; t < nkt; t += 2) {
-    step(t, lds[0], 0);
-    step(t + 1, lds[1], PF - 1);
+    step(t, lds[0]);
+    step(t + 1, lds[1]);
   }
 
-  const float inv = 1.0f / (l + half_swap(l));
-  const int i = wrow0 + lc;
-  if (i < n) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float lt = l[qb];                              // row sum over the four lane groups
+    lt += __shfl_xor(lt, 16, TSA_WAVE);
+    lt += __shfl_xor(lt, 32, TSA_WAVE);
+    const float inv = 1.0f / lt;
+    const int i = wrow0 + 16 * qb + lq;
+    if (i >= n) continue;
     if (FUSED) {
       // out = residual + O, with O first rounded to bf16 as the staged path stores it.
       const int64_t roff = (int64_t)idx_bh[i] * o_r;
       const __bf16* rrow = reinterpret_cast<const __bf16*>(p.res) + b * p.o_b + h * p.o_h + roff;
       __bf16* orow = obase + roff;
-      u32x2 rvs[D / 32][4];                       // all residual reads in flight at once
+      u32x2 rvs[D / 16];                           // all residual reads in flight at once
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) rvs[db][r4] = *reinterpret_cast<const u32x2*>(rrow + db * 32 + 8 * r4 + 4 * hf);
+      for (int db = 0; db < D / 16; ++db) rvs[db] = *reinterpret_cast<const u32x2*>(rrow + 16 * db + 4 * g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 16; ++db) {
+        float v[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + 8 * r4 + 4 * hf;
-          const u32x2 rv = rvs[db][r4];
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ob = bf16_to_f32(f32_to_bf16(o[db][4 * r4 + e] * inv));
-            const uint32_t rb = (rv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            v[e] = bf16_to_f32(rb) + ob;
-          }
-          store4<__bf16>(orow + d0, v[0], v[1], v[2], v[3]);
+        for (int e = 0; e < 4; ++e) {
+          const float ob = bf16_to_f32(f32_to_bf16(o[db][qb][e] * inv));
+          const uint32_t rb = (rvs[db][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          v[e] = bf16_to_f32(rb) + ob;
         }
+        store4<__bf16>(orow + 16 * db + 4 * g, v[0], v[1], v[2], v[3]);
+      }
     } else {
       __bf16* orow = obase + (int64_t)i * o_r;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + 8 * r4 + 4 * hf;
-          store4<__bf16>(orow + d0, o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                         o[db][4 * r4 + 3] * inv);
-        }
+      for (int db = 0; db < D / 16; ++db)
+        store4<__bf16>(orow + 16 * db + 4 * g, o[db][qb][0] * inv, o[db][qb][1] * inv, o[db][qb][2] * inv,
+                       o[db][qb][3] * inv);
     }
   }
 }
 
 template <int D, int NW, int MODE>
 hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * BF16_WQ;
   p.BH = B * H;
   p.ntiles = (p.n + BM - 1) / BM;
   int64_t blocks = (int64_t)p.BH * p.ntiles;
