@@ -387,11 +387,10 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
 // (l % 16) and the same slice.  Every K and V operand a wave reads from LDS feeds its three
 // query blocks, so a 64-key tile's LDS operand bytes serve 48 query rows per wave.
 //
-// Scores: S^T (16 keys x 16 queries) = K Q^T.  Lane group g = l/16 covers the contiguous
-// quarter d in [g*D/4, (g+1)*D/4) of the contraction (K and Q use the same split, which
-// leaves every dot product unchanged), so a lane's Q operands are its query row's quarter
-// and its K operands 16-byte reads of one key row.  The lane then owns query (l % 16) of
-// each block and keys 4g .. 4g+3 of each 16-key block.
+// Scores: S^T (16 keys x 16 queries) = K Q^T over D/32 steps of 32 d.  In step s lane
+// group g = l/16 supplies d = 32 s + 8 g .. +7 (K and Q use the same split), so the four
+// lane groups of one key row read its 64 contiguous bytes of the step.  The lane then owns
+// query (l % 16) of each block and keys 4g .. 4g+3 of each 16-key block.
 //
 // P.V: O^T (16 d x 16 queries) += V^T (16 d x 32 keys) P^T.  A lane's P^T operand is its
 // own 8 probabilities of the 32-key half, keys {4g .. 4g+3} and {16+4g .. 16+4g+3}; the V^T
@@ -402,12 +401,13 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
 // reads (k0 = 4g and 16 + 4g) make the operand.
 //
 // LDS rows are padded, not swizzled, so every operand address is one register plus an
-// immediate.  K rows are 2d+16 bytes apart: the 16 lanes of one 16-byte read cycle read
-// 16 consecutive key rows at one column, 4 banks apart.  V rows are 2d+32 bytes apart: one
-// transposing read cycle serves 32 lanes, eight key rows of 8 banks each, and rows 2d+32
-// bytes apart land 8 banks apart (2d+64, the pitch for a 32x32 operand layout, puts rows
-// four apart on the same banks).  The tile loop is unrolled by two so the buffer offsets
-// are immediates too.
+// immediate.  K and V rows are both 2d+32 bytes apart (8 banks between rows).  For V: one
+// transposing read cycle serves 32 lanes, eight key rows of 8 banks each, which this pitch
+// keeps disjoint (2d+64, the pitch for a 32x32 operand layout, puts rows four apart on the
+// same banks).  For K the pitch was chosen by the bank-conflict counter: with the 64-byte
+// row segments above it reads without conflicts, while 2d+16 and 2d+64 (and every pitch
+// with K split into contiguous quarters of d per lane group) conflict.  The tile loop is
+// unrolled by two so the buffer offsets are immediates too.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   constexpr int LOADS = BN * CPR / NT;            // chunks per lane per tensor per tile
   static_assert(LOADS >= 1 && BN * CPR % NT == 0, "a tile splits evenly over the lanes");
   constexpr int RSTEP = NT / CPR;                 // rows between a lane's chunks
-  constexpr int KP = 2 * D + 16, VP = 2 * D + 32; // padded row pitches, bytes
+  constexpr int KP = 2 * D + 32, VP = 2 * D + 32; // padded row pitches, bytes
   struct Buf {
     char k[BN * KP];
     char v[BN * VP];
@@ -562,21 +562,21 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
     next_k0 += BN;
   };
 
-  // Q operands: block qb, step s = 8 values of row wrow0 + 16 qb + lq from d = g*D/4 + 8 s.
+  // Q operands: block qb, step s = 8 values of row wrow0 + 16 qb + lq from d = 32 s + 8 g.
   bf16x8 qf[QB][ST];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 16 * qb + lq;
     if (row < n) {
-      const __bf16* src = qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + g * (D / 4);
+      const __bf16* src = qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + 8 * g;
 #pragma unroll
-      for (int s = 0; s < ST; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8*>(src + 8 * s);
+      for (int s = 0; s < ST; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < ST; ++s) qf[qb][s] = bf16x8{};
     }
   }
-  const int koff = lq * KP + g * (D / 4) * 2;                      // K operand: key lq, quarter g
+  const int koff = lq * KP + g * 16;                               // K operand: key lq, d 8g + 32 s
   const int voff = (4 * g + (lq >> 2)) * VP + 4 * (lq & 3) * 2;   // V^T operand, see above
 
   f32x4 o[D / 16][QB];
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
         bf16x8 kf[ST];
 #pragma unroll
         for (int st = 0; st < ST; ++st)
-          kf[st] = *reinterpret_cast<const bf16x8*>(cur.k + (32 * hh + 16 * kk) * KP + koff + st * 16);
+          kf[st] = *reinterpret_cast<const bf16x8*>(cur.k + (32 * hh + 16 * kk) * KP + koff + st * 64);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kk][qb] = f32x4{};
