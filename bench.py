@@ -414,6 +414,20 @@ def cpu_baseline(w, x, budget_s=20.0):
                      "numpy": np.__version__, "blas": blas}}
 
 
+def copy_bandwidth(torch, timer, reps=10):
+    """Measured HBM copy rate beside the published 8 TB/s: torch's device copy of a 1 GiB
+    tensor (1 GiB read + 1 GiB written per call, far beyond the 256 MB Infinity Cache)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = timer.run(lambda: dst.copy_(src), reps)
+    del src, dst
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"kernel": "torch copy_ of a 1 GiB device tensor", "bytes_per_call": 2 * n, "avg_ms": ms,
+            "gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -485,6 +499,10 @@ def main():
                 "kernel": "attn_bf16_kernel<128, 8, ATT_COMPACT> (tsa_attn)" if w.dtype == "bf16" else "attn_kernel<float> (tsa_attn)",
                 "avg_launch_ms": attn_ms,
                 "algorithmic_per_launch": f"2*B*H*d*keep*(keep+1) = {a['attn_flops']:.4e} flop"}
+    copy = copy_bandwidth(torch, timer)
+    for st in head["stage_roofline"].values():
+        if st["bound"] == "hbm":
+            st["frac_of_copy"] = st["achieved"] / copy["gbs"]
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
@@ -502,7 +520,7 @@ def main():
         "graph_ms_per_step": head["graph_ms_per_step"], "graph_tokens_per_s": head["graph_tokens_per_s"],
         "stage_ms": head["stage_ms"], "stage_stats_ms": head["stage_stats_ms"], "stage_rate": head["stage_rate"],
         "stage_rate_cold": head["stage_rate_cold"], "stage_roofline": head["stage_roofline"],
-        "sweep": sweep,
+        "sweep": sweep, "hbm_copy": copy,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
