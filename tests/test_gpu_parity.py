@@ -83,7 +83,10 @@ def test_gather_scatter_bitexact(dt, d):
 # ---- attention on compact rows and dense -------------------------------------------------
 
 @pytest.mark.parametrize("dt,d,n", [("bf16", 128, 1), ("bf16", 128, 31), ("bf16", 128, 300), ("bf16", 128, 1000),
-                                    ("bf16", 64, 515), ("fp32", 64, 256), ("fp32", 64, 700), ("fp32", 128, 333)])
+                                    # bf16: a wave holds 48 query rows, a workgroup 384
+                                    ("bf16", 128, 47), ("bf16", 128, 48), ("bf16", 128, 385), ("bf16", 128, 769),
+                                    ("bf16", 64, 384), ("bf16", 64, 515),
+                                    ("fp32", 64, 256), ("fp32", 64, 700), ("fp32", 128, 333)])
 def test_attn_compact(dt, d, n):
     B, H = 2, 3
     rng = np.random.default_rng(n + d)
