@@ -406,7 +406,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE) void attn_kernel(AttnParams p) {
 // keeps disjoint (2d+64, the pitch for a 32x32 operand layout, puts rows four apart on the
 // same banks).  For K the pitch was chosen by the bank-conflict counter: with the 64-byte
 // row segments above it reads without conflicts, while 2d+16 and 2d+64 (and every pitch
-// with K split into contiguous quarters of d per lane group) conflict.  The tile loop is
+// tried, 2d+16 to 2d+80, with K split into contiguous quarters of d per lane group) conflict.  The tile loop is
 // unrolled by two so the buffer offsets are immediates too.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
