@@ -496,7 +496,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic(w.name), "traffic_unit": "HBM bytes per launch",
-                "kernel": "attn_bf16_kernel<128, 8, ATT_COMPACT> (tsa_attn)" if w.dtype == "bf16" else "attn_kernel<float> (tsa_attn)",
+                "kernel": "attn_bf16_kernel<128, 8, ATT_COMPACT, 1> (tsa_attn)" if w.dtype == "bf16" else "attn_kernel<float> (tsa_attn)",
                 "avg_launch_ms": attn_ms,
                 "algorithmic_per_launch": f"2*B*H*d*keep*(keep+1) = {a['attn_flops']:.4e} flop"}
     copy = copy_bandwidth(torch, timer)

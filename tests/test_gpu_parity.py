@@ -368,9 +368,11 @@ def test_gather_scatter_per_kv_head_bitexact(dt, d):
     assert np.array_equal(host(r2), want)
 
 
-@pytest.mark.parametrize("dt,d,n", [("bf16", 128, 300), ("bf16", 128, 1000), ("bf16", 64, 257), ("fp32", 128, 200)])
-def test_attn_per_kv_head(dt, d, n):
-    B, H, Hkv = 1, 8, 2
+# bf16 with an even group size runs two query heads per workgroup on shared K/V tiles.
+@pytest.mark.parametrize("dt,d,n,B,H,Hkv", [("bf16", 128, 300, 1, 8, 2), ("bf16", 128, 1000, 1, 8, 2),
+                                           ("bf16", 128, 500, 2, 8, 4), ("bf16", 128, 400, 2, 6, 2),
+                                           ("bf16", 64, 257, 1, 8, 2), ("fp32", 128, 200, 1, 8, 2)])
+def test_attn_per_kv_head(dt, d, n, B, H, Hkv):
     rng = np.random.default_rng(n + d + 1)
     qh = rng.standard_normal((B, H, n, d)).astype(np.float32)
     kh, vh = (rng.standard_normal((B, Hkv, n, d)).astype(np.float32) for _ in range(2))
@@ -386,6 +388,7 @@ def test_attn_per_kv_head(dt, d, n):
     (1, 8, 2, 1000, 128, 400, 64, 4, False),
     (2, 8, 4, 700, 128, 300, 16, 2, True),
     (1, 4, 1, 513, 64, 200, 64, 4, False),
+    (1, 6, 2, 600, 128, 250, 32, 4, False),     # group of 3: one head per workgroup
 ])
 def test_forward_bf16_per_kv_head(B, H, Hkv, L, d, keep, W, ns, in_place):
     x = workloads.small_random(B, H, Hkv, L, d, seed=31, dtype="bf16")

@@ -13,7 +13,9 @@
 // Design for gfx950 (CDNA4):
 // * bf16: a workgroup is 8 waves (2 per SIMD, within 256 registers each, so one wave's
 //   softmax arithmetic issues while the other wave's matrix instructions run) over 384
-//   query rows of one (batch, head).  Each wave keeps 48 query rows in registers as the
+//   query rows of one (batch, head), or 192 rows of each of two query heads that read the
+//   same K/V rows (GQA with one subset per KV head, and the dense reference), which then
+//   share every staged K/V tile.  Each wave keeps 48 query rows in registers as the
 //   operands of three 16-row blocks on the 16x16x32 bf16 MFMA, so each K or V operand it
 //   reads from LDS feeds three blocks: LDS operand traffic, the kernel's main cost, per
 //   unit of matrix work is two thirds of what 32-row blocks on the 32x32x16 MFMA need.
@@ -432,12 +434,17 @@ constexpr int BF16_WQ = 16 * BF16_QB;      // query rows per wave
 // ATT_FUSED (the compact rows are read through each head's index list straight from
 // [B][L][H][d] / [B][L][Hkv][d], and the epilogue writes residual + O into those rows of
 // the output: the fused forward, which never materialises Q^, K^, V^ or O^).
-template <int D, int NW, int MODE>
+//
+// HPW = 2: the workgroup runs two query heads that read the same K/V rows (a GQA group with
+// one subset per KV head, or the dense reference), four waves each, so each staged K/V tile
+// serves both heads.
+template <int D, int NW, int MODE, int HPW>
 __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams p) {
   constexpr bool FUSED = MODE == ATT_FUSED, STRIDED = MODE != ATT_COMPACT;
   constexpr int NT = NW * TSA_WAVE;
   constexpr int QB = BF16_QB, WQ = BF16_WQ;
-  constexpr int BM = NW * WQ;
+  constexpr int WPH = NW / HPW;                   // waves per query head
+  constexpr int BM = WPH * WQ;                    // query rows per head in the tile
   constexpr int ST = D / 32;                      // MFMA steps over d
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / NT;            // chunks per lane per tensor per tile
@@ -496,8 +503,9 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
       tile = p.ntiles - 1 - bid / p.BH;
     }
   }
-  const int64_t b = bh / p.H;
-  const int h = bh % p.H;
+  // bh counts groups of HPW query heads that read the same K/V rows; this wave's head:
+  const int64_t b = bh / (p.H / HPW);
+  const int h = HPW == 1 ? (int)(bh % p.H) : (int)(bh % (p.H / HPW)) * HPW + wave / WPH;
   const int kvh = h / kv_div;
   const __bf16* qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_b + h * p.q_h;
   const char* kb8 = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_b + kvh * p.k_h);
@@ -506,7 +514,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   const int32_t* idx_bh = FUSED ? p.idx + (b * (p.H / p.idx_div) + h / p.idx_div) * (int64_t)p.n : nullptr;
 
   const int q0 = tile * BM;
-  const int wrow0 = q0 + wave * WQ;
+  const int wrow0 = q0 + (HPW == 1 ? wave : wave % WPH) * WQ;
   const int wave_last = min(n - 1, wrow0 + WQ - 1);
   const int nkt = (min(n, q0 + BM) - 1) / BN + 1;
 
@@ -732,10 +740,10 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   }
 }
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, int HPW = 1>
 hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
-  constexpr int BM = NW * BF16_WQ;
-  p.BH = B * H;
+  constexpr int BM = NW / HPW * BF16_WQ;
+  p.BH = B * H / HPW;                             // head groups (the adaptive paths run HPW = 1)
   p.ntiles = (p.n + BM - 1) / BM;
   int64_t blocks = (int64_t)p.BH * p.ntiles;
   if (MODE == ATT_FUSED && p.counts && p.plan) {
@@ -744,7 +752,7 @@ hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
                                                 p.plan_cap);
     blocks = 8ll * p.plan_cap * p.ntiles;
   }
-  attn_bf16_kernel<D, NW, MODE><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
+  attn_bf16_kernel<D, NW, MODE, HPW><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -761,8 +769,10 @@ hipError_t launch_attn_t(AttnParams p, int B, int H, hipStream_t s) {
 template <bool DENSE>
 hipError_t dispatch_attn(const tsa_desc& d, AttnParams p, hipStream_t s) {
   if (d.dtype == TSA_BF16) {
-    if (d.d == 128) return launch_attn_bf16<128, 8, DENSE ? ATT_DENSE : ATT_COMPACT>(p, d.B, d.H, s);
-    if (d.d == 64) return launch_attn_bf16<64, 8, DENSE ? ATT_DENSE : ATT_COMPACT>(p, d.B, d.H, s);
+    constexpr int M = DENSE ? ATT_DENSE : ATT_COMPACT;
+    const bool pairs = p.kv_div % 2 == 0;         // two query heads per K/V head and workgroup
+    if (d.d == 128) return pairs ? launch_attn_bf16<128, 8, M, 2>(p, d.B, d.H, s) : launch_attn_bf16<128, 8, M>(p, d.B, d.H, s);
+    if (d.d == 64) return pairs ? launch_attn_bf16<64, 8, M, 2>(p, d.B, d.H, s) : launch_attn_bf16<64, 8, M>(p, d.B, d.H, s);
   } else {
     if (d.d == 128) return launch_attn_t<float, 128, 1, 4, DENSE>(p, d.B, d.H, s);
     if (d.d == 64) return launch_attn_t<float, 64, 1, 4, DENSE>(p, d.B, d.H, s);
@@ -810,8 +820,13 @@ hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, co
   p.k_r = (int64_t)d.Hkv * d.d; p.k_h = d.d; p.k_b = (int64_t)d.L * d.Hkv * d.d;
   p.o_r = p.q_r; p.o_h = p.q_h; p.o_b = p.q_b;
   p.c = attn_c(d);
-  if (d.d == 128) return launch_attn_bf16<128, 8, ATT_FUSED>(p, d.B, d.H, s);
-  if (d.d == 64) return launch_attn_bf16<64, 8, ATT_FUSED>(p, d.B, d.H, s);
+  // Two query heads per workgroup when they share a subset (and so K/V rows); adaptive
+  // budgets keep one head per workgroup (the per-XCD plan deals heads).
+  const bool pairs = !counts && p.idx_div % 2 == 0 && p.kv_div % 2 == 0;
+  if (d.d == 128)
+    return pairs ? launch_attn_bf16<128, 8, ATT_FUSED, 2>(p, d.B, d.H, s) : launch_attn_bf16<128, 8, ATT_FUSED>(p, d.B, d.H, s);
+  if (d.d == 64)
+    return pairs ? launch_attn_bf16<64, 8, ATT_FUSED, 2>(p, d.B, d.H, s) : launch_attn_bf16<64, 8, ATT_FUSED>(p, d.B, d.H, s);
   return hipErrorInvalidValue;
 }
 
