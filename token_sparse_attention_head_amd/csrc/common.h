@@ -52,11 +52,6 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, TSA_WAVE);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, TSA_WAVE));
-  return v;
-}
-
 // ---- MFMA wrappers ---------------------------------------------------------------------
 // 32x32 output tiles.  Lane l holds output column (l % 32) and rows
 // 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.  Operand A: lane l supplies row (l % 32);
