@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-configs", action="store_true", help="skip the other workloads (C1-C3, C5)")
     p.add_argument("--stage-reps", type=int, default=5)
     p.add_argument("--stage", choices=["score", "select", "gather", "attn", "scatter", "dense", "forward", "drift",
                                        "copy"],
@@ -490,6 +491,23 @@ def main():
             f"fixed budget with the same work {json.dumps(res['fixed_budget_same_work'])}")
         sweep.append(res)
 
+    # The other configurations of the workload set (parity cases; reported, not the headline).
+    configs = []
+    if not args.no_configs and not args.no_sweep:
+        for name in ("fp32_L512", "bf16_L8k_r0.5", "bf16_L32k_r0.25", "bf16_L64k_planted"):
+            wi = workloads.WORKLOADS[name]
+            xi = workloads.make_inputs(wi)
+            res = gpu_case(tsa, torch, timer, wi, xi, args, args.stage_reps, max(3, args.steps // 2), 1,
+                           name == "bf16_L32k_r0.25" and not args.no_dense)
+            del xi
+            keys = ("workload", "keep", "ratio", "ms_per_step", "tokens_per_s", "graph_ms_per_step", "stage_ms",
+                    "stage_roofline", "dense_ms", "speedup_vs_dense", "attn_speedup_vs_dense")
+            entry = {k: res[k] for k in keys if k in res}
+            entry["shape"] = {"B": wi.B, "L": wi.L, "H": wi.H, "Hkv": wi.Hkv, "d": wi.d, "W": wi.W,
+                              "n_sink": wi.n_sink, "dtype": wi.dtype}
+            log(f"{name}: {res['ms_per_step']:.3f} ms/step, stages {json.dumps(res['stage_ms'])}")
+            configs.append(entry)
+
     a = algorithmic(w)
     attn_ms = head["stage_ms"]["attn"]
     achieved = a["attn_flops"] / (attn_ms * 1e-3) / 1e12
@@ -520,7 +538,7 @@ def main():
         "graph_ms_per_step": head["graph_ms_per_step"], "graph_tokens_per_s": head["graph_tokens_per_s"],
         "stage_ms": head["stage_ms"], "stage_stats_ms": head["stage_stats_ms"], "stage_rate": head["stage_rate"],
         "stage_rate_cold": head["stage_rate_cold"], "stage_roofline": head["stage_roofline"],
-        "sweep": sweep, "hbm_copy": copy,
+        "sweep": sweep, "configs": configs, "hbm_copy": copy,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
