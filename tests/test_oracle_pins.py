@@ -170,6 +170,46 @@ def test_select_edge_cases():
         oracle.select_row(s, 11, 3, 2)                                           # keep > L
 
 
+def test_threshold_hand_case():
+    # L = 10, W = 2, one sink: F = {0, 8, 9}, and the forced positions score highest, so a
+    # threshold that counted them would come out too high.  The candidates 1..7 score
+    # 5, 3, 5, 1, 5, 0, 2, so the taken scores in order are 5, 5, 5, 3, 2, 1, 0.
+    s = np.array([9.0, 5.0, 3.0, 5.0, 1.0, 5.0, 0.0, 2.0, 7.0, 8.0])
+    assert oracle.threshold(s, 3, 2, 1) == math.inf           # keep = |F|: no candidate taken
+    assert oracle.threshold(s, 4, 2, 1) == 5.0                # first of three tied 5s
+    assert oracle.threshold(s, 6, 2, 1) == 5.0                # last of the tied 5s
+    assert oracle.threshold(s, 7, 2, 1) == 3.0
+    assert oracle.threshold(s, 9, 2, 1) == 1.0
+    assert oracle.threshold(s, 10, 2, 1) == 0.0               # keep = L: the lowest candidate
+    # The threshold is the lowest score among the non-forced positions the select takes.
+    for keep in range(4, 11):
+        S = oracle.select_row(s, keep, 2, 1)
+        taken = [p for p in S if p not in (0, 8, 9)]
+        assert oracle.threshold(s, keep, 2, 1) == min(s[taken])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_threshold_brute_force(seed):
+    # Brute force by counting: theta is the largest candidate score t such that at least
+    # keep - |F| candidates score t or more (no sort, no select involved).
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(5, 30))
+    W = int(rng.integers(1, 5))
+    n_sink = int(rng.integers(0, 4))
+    F = set(oracle.forced_positions(L, W, n_sink).tolist())
+    cand = [p for p in range(L) if p not in F]
+    s = np.round(rng.random(L) * 6) / 6                        # many ties
+    for p in F:
+        s[p] = 2.0 + rng.random()                              # forced positions score above every candidate
+    for keep in range(len(F), L + 1):
+        n = keep - len(F)
+        if n == 0:
+            want = math.inf
+        else:
+            want = max(t for t in (s[p] for p in cand) if sum(s[u] >= t for u in cand) >= n)
+        assert oracle.threshold(s, keep, W, n_sink) == want, (keep, n)
+
+
 def test_gather_scatter_brute_force():
     x = workloads.small_random(2, 4, 2, 9, 3, seed=5)
     idx = np.array([[[0, 2, 5, 8], [1, 2, 3, 8], [0, 4, 7, 8], [3, 5, 6, 8]]] * 2)
