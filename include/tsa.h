@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 3
+#define TSA_ABI_VERSION 4
 #define TSA_MAX_W 64 /* largest score window the scoring kernel holds in registers */
 
 typedef enum {
@@ -86,7 +86,14 @@ typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
 typedef enum { TSA_SUBSETS_PER_HEAD = 0, TSA_SUBSETS_PER_KV_HEAD = 1 } tsa_subsets;
 
 /* Which call a workspace is sized for. */
-typedef enum { TSA_OP_SCORE = 0, TSA_OP_SELECT = 1, TSA_OP_SCATTER = 2, TSA_OP_FORWARD = 3, TSA_OP_DRIFT = 4 } tsa_op;
+typedef enum {
+  TSA_OP_SCORE = 0,
+  TSA_OP_SELECT = 1,
+  TSA_OP_SCATTER = 2,
+  TSA_OP_FORWARD = 3,
+  TSA_OP_DRIFT = 4,
+  TSA_OP_SPARSE_ATTN = 5
+} tsa_op;
 
 typedef struct {
   int32_t B, H, Hkv, L, d;
@@ -186,6 +193,25 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
                        const void* residual, void* out, float* scores_opt, int32_t* idx_opt,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Compress, attend and decompress on given subsets (the paper page's Figure 3, stages 1
+ * and 2; skill page, Steps 2 and 3): for every query head h with subset r(h) and its
+ * K_r kept rows,
+ *   out[b][p][h] = residual[b][p][h] + O[b][h][t]   if p = idx[b][r(h)][t], t < K_r,
+ *   out[b][p][h] = residual[b][p][h]                (bit-exact) otherwise,
+ * with O the causal attention of tsa_attn over the rows q, k, v hold at the subset's
+ * positions, rounded to dtype, and residual + O summed in fp32 and rounded once: exactly
+ * what tsa_gather_qkv -> tsa_attn -> tsa_scatter_residual produce.  idx [B][R][keep] as
+ * tsa_select writes it: ascending positions in [0, L), then (tau > 0 only) -1 padding;
+ * the row counts K_r are read off the padding.  bf16 runs one attention kernel that
+ * reads the rows through idx and writes residual + O into the kept rows (no compact
+ * tensors); an out-of-place output first gets the residual at the positions no head
+ * keeps.  fp32 runs the three stages through compact tensors in the workspace.  out ==
+ * residual (the same pointer) updates in place; any other overlap of out with an input
+ * is TSA_ERR_ALIAS.  Positions outside [0, L) in a kept row give unspecified results but
+ * no access outside the tensors.  Workspace: TSA_OP_SPARSE_ATTN. */
+tsa_status tsa_sparse_attn(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* residual, void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Dense causal attention over all L positions with grouped-query heads, the library's
  * own full-attention reference (the paper page's Abstract: the method composes with
  * dense attention kernels).  o[b][i][h] = sum over j <= i of
@@ -207,6 +233,13 @@ tsa_status tsa_dense_attn(const tsa_desc* desc, const void* q, const void* k, co
  * drifts is below 0.1 (host logic, not part of the library). */
 tsa_status tsa_drift(const tsa_desc* desc, const void* a, const void* b, double* drift,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Plain device copy of `bytes` bytes (a multiple of 16; src and dst 16-byte aligned and
+ * not overlapping), streamed with non-temporal 16-byte loads and stores.  Not a step of
+ * the method: it is the measured bandwidth reference that the library's data-movement
+ * kernels (gather, scatter, the copy of unkept rows, drift) are compared with, and the
+ * calibration kernel of hardware byte counters. */
+tsa_status tsa_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

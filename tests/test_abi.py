@@ -11,8 +11,8 @@ tsa = ensure_built()
 L = tsa.lib()
 
 EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_budget", "tsa_check", "tsa_dense_attn", "tsa_drift",
-            "tsa_forward", "tsa_gather_qkv",
-            "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_status_str", "tsa_workspace_size"]
+            "tsa_forward", "tsa_gather_qkv", "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_sparse_attn",
+            "tsa_status_str", "tsa_stream_copy", "tsa_workspace_size"]
 
 
 def D(**kw):
@@ -27,7 +27,7 @@ def test_header_declares_and_library_exports_every_entry_point():
     assert declared == EXPECTED
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tsa_abi_version() == 3
+    assert L.tsa_abi_version() == 4
     assert L.tsa_status_str(7) and L.tsa_status_str(1234) == b"unknown status"
 
 
@@ -90,6 +90,11 @@ def test_workspace_sizes():
     # drift: partial sums only, sized by B*L; the budget fields are not looked at
     assert 0 < tsa.tsa_workspace_size(D(keep=3), tsa.TSA_OP_DRIFT) <= 2048 * 8
     assert tsa.tsa_workspace_size(D(L=0, keep=0), tsa.TSA_OP_DRIFT) == 0
+    # sparse attention on given subsets: bf16 needs the inverse map only (plus row counts and
+    # the per-XCD plan with adaptive budgets); fp32 also holds the four compact tensors
+    assert tsa.tsa_workspace_size(d, tsa.TSA_OP_SPARSE_ATTN) == 32 * 8192 * 4
+    assert tsa.tsa_workspace_size(ad, tsa.TSA_OP_SPARSE_ATTN) > 32 * 8192 * 4 + 32 * 4
+    assert tsa.tsa_workspace_size(D(dtype=tsa.TSA_F32), tsa.TSA_OP_SPARSE_ATTN) >= 4 * 32 * 4096 * 128 * 4
 
 
 A = 1 << 40           # fake, well-separated, 16-byte aligned addresses
@@ -156,6 +161,22 @@ def test_entry_points_reject_before_launch():
     assert call("tsa_drift", bd, q, r, o, r + 4096, big, None) == 7
     assert call("tsa_drift", ctypes.byref(D(keep=2)), q, r, o, ws, 16, None) == 6   # budget not checked
     assert call("tsa_drift", ctypes.byref(D(d=96)), q, r, o, ws, big, None) == 2
+    # sparse attention on given subsets
+    sa = "tsa_sparse_attn"
+    assert call(sa, bd, q, k, v, None, r, o, ws, big, None) == 1
+    assert call(sa, bd, q, k, v, idx, r, o, None, 0, None) == 6
+    assert call(sa, bd, q, k, v, idx, r, o, ws, 16, None) == 6
+    assert call(sa, bd, q, k, v, idx + 4, r, o, ws, big, None) == 5
+    assert call(sa, bd, q, k, v, idx, r, q, ws, big, None) == 7            # out over q
+    assert call(sa, bd, q, k, v, idx, r, r + 256, ws, big, None) == 7      # partial overlap with the residual
+    assert call(sa, bd, q, k, v, idx, r, o, idx + 64, big, None) == 7      # workspace over idx
+    assert call(sa, ctypes.byref(D(keep=2)), q, k, v, idx, r, o, ws, big, None) == 3
+    # plain copy
+    assert call("tsa_stream_copy", o, None, 4096, None) == 1
+    assert call("tsa_stream_copy", o, q, 4095, None) == 5
+    assert call("tsa_stream_copy", o + 8, q, 4096, None) == 5
+    assert call("tsa_stream_copy", q + 2048, q, 4096, None) == 7
+    assert call("tsa_stream_copy", None, None, 0, None) == 0               # nothing to copy
     # descriptor errors come first
     bad = ctypes.byref(D(keep=2))
     assert call("tsa_forward", bad, q, k, v, r, o, None, None, ws, big, None) == 3

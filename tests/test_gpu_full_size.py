@@ -96,7 +96,7 @@ def test_full_bf16_L32k_r025():
     _check(w, x, heads=[(0, 2), (0, 19)])
 
 
-@pytest.mark.parametrize("name", ["bf16_L128k_r0.1", "bf16_L128k_r0.5"])
+@pytest.mark.parametrize("name", ["bf16_L128k_r0.1", "bf16_L128k_r0.25", "bf16_L128k_r0.5"])
 def test_full_bf16_L128k(name):
     w, x = _inputs(name)
     _check(w, x, heads=[(0, 0), (0, 30)], rows_per_head=8)
@@ -214,3 +214,87 @@ def test_full_adaptive_graded_L128k():
     print(f"{w.name}: score rel err {worst_s:.2e}, out excess {worst_out:.2e}")
     assert worst_s <= 1e-5
     assert worst_out <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", ["bf16_L32k_r0.25", "bf16_L128k_r0.5"])
+def test_full_dense_attention_sampled_rows(name):
+    # The library's dense causal attention (the denominator of every speedup figure) at
+    # L = 32768 and L = 131072: sampled rows of sampled heads against the oracle's
+    # attention with every position kept (keep = L: the subset is the whole sequence).
+    w, x = _inputs(name)
+    q, k, v = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkv")
+    o = tsa.dense_attn(q, k, v)
+    torch.cuda.synchronize()
+    B, L, H, d = x["q"].shape
+    G = H // w.Hkv
+    scale = 1.0 / np.sqrt(d)
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for b, h in [(0, 0), (0, 13), (0, 31)]:
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, L - 1], rng.integers(0, L, 6)]))
+        want = oracle.attend_rows(x["q"][b, :, h, :], x["k"][b, :, h // G, :], x["v"][b, :, h // G, :], rows, scale)
+        got = o[b, torch.from_numpy(rows).cuda(), h, :].float().cpu().numpy().astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(got - want))))
+    print(f"{name} dense attention: max abs err {worst:.2e} on sampled rows")
+    assert worst <= TOL["bf16"]
+
+
+def test_full_compact_attention_n65536():
+    # tsa_attn on the compact rows of the L = 131072 keep 0.5 layer (n = 65536 rows per
+    # head): sampled rows of two heads against the oracle on the same subsets.
+    w, x = _inputs("bf16_L128k_r0.5")
+    q, k, v, r = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkvr")
+    _, _, ig = tsa.forward(q, k, v, r, w.keep, w.W, w.n_sink, return_scores=True)
+    oh = tsa.attn(*tsa.gather_qkv(q, k, v, ig))
+    torch.cuda.synchronize()
+    idx_all = ig.cpu().numpy().astype(np.int64)
+    d = w.d
+    scale = 1.0 / np.sqrt(d)
+    rng = np.random.default_rng(12)
+    worst = 0.0
+    for b, h in [(0, 4), (0, 27)]:
+        g = h // w.G
+        idx = idx_all[b, h]
+        rows = np.unique(np.concatenate([[0, 383, 384, w.keep - 1], rng.integers(0, w.keep, 6)]))
+        want = oracle.attend_rows(x["q"][b, idx, h, :], x["k"][b, idx, g, :], x["v"][b, idx, g, :], rows, scale)
+        got = oh[b, h, torch.from_numpy(rows).cuda(), :].float().cpu().numpy().astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(got - want))))
+    print(f"compact attention n = {w.keep}: max abs err {worst:.2e} on sampled rows")
+    assert worst <= TOL["bf16"]
+
+
+def test_full_sparse_attn_in_place_equals_forward():
+    # The launch the benchmark times for the attention roofline: tsa_sparse_attn in place
+    # on the subsets tsa_forward chose (one fused attention kernel) writes what the forward
+    # wrote, over the whole L = 131072 tensor.
+    w, x = _inputs("bf16_L128k_r0.5")
+    q, k, v, r = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkvr")
+    out, _, ig = tsa.forward(q, k, v, r, w.keep, w.W, w.n_sink, return_scores=True)
+    r2 = r.clone()
+    tsa.sparse_attn(q, k, v, ig, r2, out=r2)
+    torch.cuda.synchronize()
+    assert torch.equal(r2, out)
+
+
+def test_full_graded_fixed_budget_selection():
+    # Sharp logits (query scale up to 4 on the graded workload) with a fixed budget of half
+    # the positions: the GPU subsets may differ from the subsets of the float64 oracle
+    # scores only at near-ties (relative gap 1e-6), checked on the sharpest, a middle and
+    # the most diffuse head.
+    w, x = _inputs("bf16_L128k_tau0.2_graded")
+    keep = w.L // 2
+    q, k, v, r = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkvr")
+    _, sg, ig = tsa.forward(q, k, v, r, keep, w.W, w.n_sink, return_scores=True)
+    torch.cuda.synchronize()
+    s_gpu = sg.cpu().numpy().astype(np.float64)
+    idx_all = ig.cpu().numpy().astype(np.int64)
+    scale = 1.0 / np.sqrt(w.d)
+    worst_s, n_diff = 0.0, 0
+    for h in (31, 16, 0):
+        g = h // w.G
+        s_or = oracle.score_head(x["q"][0, :, h, :].astype(np.float64), x["k"][0, :, g, :].astype(np.float64),
+                                 w.W, scale)
+        worst_s = max(worst_s, rel_err(s_gpu[0, h], s_or))
+        assert np.array_equal(idx_all[0, h], oracle.select_row(s_gpu[0, h], keep, w.W, w.n_sink))
+        n_diff += check_selection(s_or[None, None], idx_all[0, h][None, None], keep, w.W, w.n_sink)
+    print(f"graded fixed budget keep {keep}: score rel err {worst_s:.2e}, subset differences {n_diff}")

@@ -151,6 +151,29 @@ FwdLayout fwd_layout(const tsa_desc& d) {
   return f;
 }
 
+// Workspace of tsa_sparse_attn: the inverse map (out-of-place output), the row counts and
+// per-XCD plan of adaptive budgets, and for fp32 the compact tensors of the staged path.
+struct SparseLayout {
+  size_t inv, counts, plan, qh, kh, vh, oh, total;
+};
+
+SparseLayout sparse_layout(const tsa_desc& d) {
+  const Sizes z = sizes_of(d);
+  const size_t comp = fused_forward(d) ? 0 : round_up(z.compact);
+  const size_t kvc = fused_forward(d) ? 0 : round_up(z.kvc);
+  SparseLayout y;
+  size_t o = 0;
+  y.inv = o; o += round_up(z.inv);
+  y.counts = o; o += d.tau > 0.f ? round_up(z.counts) : 0;
+  y.plan = o; o += d.tau > 0.f && fused_forward(d) ? round_up(tsa::attn_plan_bytes(d)) : 0;
+  y.qh = o; o += comp;
+  y.kh = o; o += kvc;
+  y.vh = o; o += kvc;
+  y.oh = o; o += comp;
+  y.total = o;
+  return y;
+}
+
 template <typename P>
 P* at(void* base, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(base) + off);
@@ -194,6 +217,7 @@ tsa_status tsa_workspace_size(const tsa_desc* desc, int op, size_t* bytes) {
     case TSA_OP_SELECT: *bytes = round_up(z.sel); break;
     case TSA_OP_SCATTER: *bytes = round_up(z.inv); break;
     case TSA_OP_FORWARD: *bytes = fwd_layout(*desc).total; break;
+    case TSA_OP_SPARSE_ATTN: *bytes = sparse_layout(*desc).total; break;
     default: return TSA_ERR_ARG;
   }
   return TSA_OK;
@@ -356,6 +380,57 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   return after_launch(tsa::launch_scatter_residual(d, oh, inv, residual, out, s), s);
 }
 
+tsa_status tsa_sparse_attn(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* residual, void* out, void* ws, size_t ws_bytes, void* stream) {
+  TSA_TRY(check_full(desc));
+  const tsa_desc& d = *desc;
+  if (empty_problem(d)) return TSA_OK;
+  if (!q || !k || !v || !idx || !residual || !out) return TSA_ERR_NULL;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(idx) || !aligned(residual) || !aligned(out) ||
+      !aligned(ws))
+    return TSA_ERR_ALIGN;
+  const Sizes z = sizes_of(d);
+  const SparseLayout y = sparse_layout(d);
+  if (!ws || ws_bytes < y.total) return TSA_ERR_WORKSPACE;
+  const Range ro{out, z.q}, rw{ws, y.total};
+  const Range ins[5] = {{q, z.q}, {k, z.kv}, {v, z.kv}, {idx, z.idx}, {residual, z.q}};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(rw, ins[i])) return TSA_ERR_ALIAS;
+    if (i < 4 && overlap(ro, ins[i])) return TSA_ERR_ALIAS;
+  }
+  const bool in_place = out == residual;
+  if (!in_place && overlap(ro, ins[4])) return TSA_ERR_ALIAS;
+  if (overlap(ro, rw)) return TSA_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* counts = nullptr;
+  if (d.tau > 0.f) {
+    counts = at<int32_t>(ws, y.counts);
+    TSA_TRY(after_launch(tsa::launch_row_counts(d, idx, counts, s), s));
+  }
+  int32_t* inv = at<int32_t>(ws, y.inv);
+  if (fused_forward(d)) {
+    if (!in_place) {
+      TSA_TRY(after_launch(tsa::launch_build_inverse(d, idx, inv, s), s));
+      TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
+    }
+    if (d.keep == 0) return TSA_OK;
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, y.plan), residual, out, s),
+                        s);
+  }
+  void* qh = at<char>(ws, y.qh);
+  void* kh = at<char>(ws, y.kh);
+  void* vh = at<char>(ws, y.vh);
+  void* oh = at<char>(ws, y.oh);
+  if (d.keep > 0) {
+    TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));
+    TSA_TRY(after_launch(launch_attn_compact(d, qh, kh, vh, oh, s), s));
+  }
+  if (in_place) return after_launch(tsa::launch_scatter_inplace(d, oh, idx, out, s), s);
+  TSA_TRY(after_launch(tsa::launch_build_inverse(d, idx, inv, s), s));
+  return after_launch(tsa::launch_scatter_residual(d, oh, inv, residual, out, s), s);
+}
+
 tsa_status tsa_dense_attn(const tsa_desc* desc, const void* q, const void* k, const void* v, void* o, void* stream) {
   TSA_TRY(check_shape(desc));
   const tsa_desc& d = *desc;
@@ -385,6 +460,15 @@ tsa_status tsa_drift(const tsa_desc* desc, const void* a, const void* b, double*
     return TSA_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(tsa::launch_drift(d, a, b, drift, static_cast<double*>(ws), s), s);
+}
+
+tsa_status tsa_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return TSA_OK;
+  if (!dst || !src) return TSA_ERR_NULL;
+  if (!aligned(dst) || !aligned(src) || bytes % 16 != 0) return TSA_ERR_ALIGN;
+  if (overlap({dst, bytes}, {src, bytes})) return TSA_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(tsa::launch_stream_copy(dst, src, bytes, s), s);
 }
 
 }  // extern "C"

@@ -68,6 +68,7 @@ struct AttnParams {
   const int32_t* counts;   // fused forward with adaptive budgets: rows of each subset [B][H / idx_div], or NULL
   const int32_t* plan;     // with counts: the per-XCD head lists of attn_plan_kernel, or NULL
   int plan_cap;            // heads per XCD list in the plan
+  int L;                   // fused forward: sequence length (index-list entries are clamped below it)
 };
 
 // Plan of the fused attention under adaptive budgets (rows differ per head).  A head's
@@ -512,6 +513,8 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   const char* vb8 = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.k_b + kvh * p.k_h);
   __bf16* obase = reinterpret_cast<__bf16*>(p.o) + b * p.o_b + h * p.o_h;
   const int32_t* idx_bh = FUSED ? p.idx + (b * (p.H / p.idx_div) + h / p.idx_div) * (int64_t)p.n : nullptr;
+  // Index-list entries are clamped to the sequence, so a corrupt list stays in bounds.
+  const uint32_t lmax = FUSED ? (uint32_t)(p.L - 1) : 0u;
 
   const int q0 = tile * BM;
   const int wrow0 = q0 + (HPW == 1 ? wave : wave % WPH) * WQ;
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint32_t off = (uint32_t)pcur[i] * rbytes + lch * 16;
+        const uint32_t off = min((uint32_t)pcur[i], lmax) * rbytes + lch * 16;
         kst[i] = ld16(kb8 + off);
         vst[i] = ld16(vb8 + off);
       }
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 16 * qb + lq;
     if (row < n) {
-      const __bf16* src = qbase + (int64_t)(FUSED ? idx_bh[row] : row) * q_r + 8 * g;
+      const __bf16* src = qbase + (int64_t)(FUSED ? min((uint32_t)idx_bh[row], lmax) : (uint32_t)row) * q_r + 8 * g;
 #pragma unroll
       for (int s = 0; s < ST; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
     } else {
@@ -712,7 +715,7 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
     if (i >= n) continue;
     if (FUSED) {
       // out = residual + O, with O first rounded to bf16 as the staged path stores it.
-      const int64_t roff = (int64_t)idx_bh[i] * o_r;
+      const int64_t roff = (int64_t)min((uint32_t)idx_bh[i], lmax) * o_r;
       const __bf16* rrow = reinterpret_cast<const __bf16*>(p.res) + b * p.o_b + h * p.o_h + roff;
       __bf16* orow = obase + roff;
       u32x2 rvs[D / 16];                           // all residual reads in flight at once
@@ -814,6 +817,7 @@ hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, co
   p.plan = attn_plan_bytes(d) ? plan : nullptr;
   p.idx_div = heads_per_subset(d);
   p.n = d.keep;
+  p.L = d.L;
   p.H = d.H;
   p.kv_div = d.H / d.Hkv;
   p.q_r = (int64_t)d.H * d.d; p.q_h = d.d; p.q_b = (int64_t)d.L * d.H * d.d;

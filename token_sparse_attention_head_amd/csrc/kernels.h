@@ -51,6 +51,10 @@ hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, co
                              const int32_t* counts, int32_t* plan, const void* res, void* out, hipStream_t s);
 // Copies residual to out at the positions a head does not keep (inverse map < 0).
 hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s);
+// Rows of every subset from an index list (first -1 entry, keep when there is none) into counts [B][R].
+hipError_t launch_row_counts(const tsa_desc& d, const int32_t* idx, int32_t* counts, hipStream_t s);
+// Plain device copy of bytes (a multiple of 16) from src to dst.
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_attn_dense(const tsa_desc& d, const void* q, const void* k, const void* v, void* o,
                              hipStream_t s);
 hipError_t launch_build_inverse(const tsa_desc& d, const int32_t* idx, int32_t* inv, hipStream_t s);

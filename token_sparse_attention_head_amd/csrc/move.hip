@@ -76,9 +76,8 @@ __device__ __forceinline__ u32x4 add_rows(u32x4 r, u32x4 o, tsa_dtype dt) {
 }
 
 // Out-of-place: one pass over [B][L][H] rows in memory order.  inv[b][r][p] is the
-// compact row of position p in subset r, or -1; head h uses subset h / SG.  SKIP_KEPT leaves kept rows untouched (the fused
-// forward writes them from its attention epilogue).
-template <int ROWB, tsa_dtype DT, bool SKIP_KEPT = false>
+// compact row of position p in subset r, or -1; head h uses subset h / SG.
+template <int ROWB, tsa_dtype DT>
 __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __restrict__ oh,
                                                                const int32_t* __restrict__ inv,
                                                                const char* __restrict__ res, char* __restrict__ out,
@@ -93,10 +92,9 @@ __global__ __launch_bounds__(256) void scatter_residual_kernel(const char* __res
   const int h = row % H;
   const int64_t off = ((b * L + p) * H + h) * ROWB + c * 16;
   const int t = inv[(b * (H / SG) + h / SG) * L + p];
-  if (SKIP_KEPT && t >= 0) return;
   const u32x4 r = ld16_nt(res + off);
   u32x4 o = r;
-  if (!SKIP_KEPT && t >= 0) o = add_rows(r, ld16(oh + (((b * H + h) * keep + t) * ROWB + c * 16)), DT);
+  if (t >= 0) o = add_rows(r, ld16(oh + (((b * H + h) * keep + t) * ROWB + c * 16)), DT);
   st16_nt(out + off, o);
 }
 
@@ -118,6 +116,110 @@ __global__ __launch_bounds__(256) void scatter_add_inplace_kernel(const char* __
   if ((unsigned)p >= (unsigned)L) return;       // padding entry
   char* dst = out + ((b * L + p) * H + h) * ROWB + c * 16;
   st16(dst, add_rows(ld16(dst), ld16(oh + crow * ROWB + c * 16), DT));
+}
+
+// Out of place, fused forward: the residual rows no head keeps, copied to out (the kept
+// rows are written by the attention epilogue).  A workgroup takes CU_ROWS consecutive
+// rows of one batch entry in memory order (row = p * H + h), reads their inverse-map
+// entries, lists the unkept rows in LDS in memory order, then copies the listed rows
+// 16 bytes per lane with CU_UNROLL loads in flight per lane: every lane has work whatever
+// the keep ratio, and enough bytes are in flight to cover the memory latency.
+constexpr int CU_THREADS = 256;
+constexpr int CU_ROWS = 1024;
+constexpr int CU_UNROLL = 8;
+
+template <int ROWB>
+__global__ __launch_bounds__(CU_THREADS) void copy_unkept_kernel(const int32_t* __restrict__ inv,
+                                                                 const char* __restrict__ res,
+                                                                 char* __restrict__ out, int H, int SG, int L) {
+  constexpr int CH = ROWB / 16;
+  constexpr int WAVES = CU_THREADS / TSA_WAVE;
+  __shared__ uint16_t list[CU_ROWS];
+  __shared__ uint32_t wave_n[CU_ROWS / TSA_WAVE];
+  const int64_t b = blockIdx.y;
+  const uint32_t nrows = (uint32_t)L * (uint32_t)H;
+  const uint32_t r0 = blockIdx.x * (uint32_t)CU_ROWS;
+  const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
+  const int32_t* inv_b = inv + b * (H / SG) * (int64_t)L;
+  bool unkept[CU_ROWS / CU_THREADS];
+#pragma unroll
+  for (int k = 0; k < CU_ROWS / CU_THREADS; ++k) {
+    const uint32_t row = r0 + k * CU_THREADS + threadIdx.x;
+    bool u = false;
+    if (row < nrows) {
+      const uint32_t p = row / H, h = row % H;
+      u = inv_b[(int64_t)(h / SG) * L + p] < 0;
+    }
+    unkept[k] = u;
+    const uint64_t m = __ballot(u);
+    if (lane == 0) wave_n[k * WAVES + wave] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // Exclusive prefix over the groups (k, wave) in memory order; every lane sums the few
+  // group counts before its own.
+  uint32_t total = 0;
+#pragma unroll
+  for (int k = 0; k < CU_ROWS / CU_THREADS; ++k) {
+    const int grp = k * WAVES + wave;
+    uint32_t before = 0;
+    for (int q = 0; q < grp; ++q) before += wave_n[q];
+    const uint64_t m = __ballot(unkept[k]);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (unkept[k]) list[before + rank] = (uint16_t)(k * CU_THREADS + threadIdx.x);
+  }
+  for (int q = 0; q < CU_ROWS / TSA_WAVE; ++q) total += wave_n[q];
+  __syncthreads();
+  const uint32_t nchunks = total * CH;
+  const int64_t base = ((int64_t)b * nrows + r0) * ROWB;
+  for (uint32_t e0 = 0; e0 < nchunks; e0 += CU_THREADS * CU_UNROLL) {
+    u32x4 v[CU_UNROLL];
+    int64_t off[CU_UNROLL];
+#pragma unroll
+    for (int i = 0; i < CU_UNROLL; ++i) {
+      const uint32_t e = e0 + i * CU_THREADS + threadIdx.x;
+      off[i] = e < nchunks ? base + (int64_t)list[e / CH] * ROWB + (e % CH) * 16 : -1;
+      if (off[i] >= 0) v[i] = ld16_nt(res + off[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CU_UNROLL; ++i)
+      if (off[i] >= 0) st16_nt(out + off[i], v[i]);
+  }
+}
+
+// Plain device copy of n16 16-byte vectors, grid-stride with CU_UNROLL vectors in flight per
+// lane: the bandwidth reference the data-movement kernels are measured against.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e0 = blockIdx.x * 256ll + threadIdx.x; e0 < n16; e0 += stride * CU_UNROLL) {
+    u32x4 v[CU_UNROLL];
+#pragma unroll
+    for (int i = 0; i < CU_UNROLL; ++i) {
+      const int64_t e = e0 + i * stride;
+      if (e < n16) v[i] = __builtin_nontemporal_load(src + e);
+    }
+#pragma unroll
+    for (int i = 0; i < CU_UNROLL; ++i) {
+      const int64_t e = e0 + i * stride;
+      if (e < n16) __builtin_nontemporal_store(v[i], dst + e);
+    }
+  }
+}
+
+// Rows of each subset from an index list written by the select: idx rows hold the kept
+// positions (>= 0) and then -1 padding, so the count is the first negative entry
+// (binary search), keep when there is none.
+__global__ __launch_bounds__(256) void row_count_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
+                                                        int rows, int keep) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int32_t* row = idx + (int64_t)r * keep;
+  int lo = 0, hi = keep;            // first t in [lo, hi] with row[t] < 0 (hi = keep: none)
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < 0) hi = mid; else lo = mid + 1;
+  }
+  counts[r] = lo;
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(int32_t* __restrict__ p, int64_t n, int32_t value) {
@@ -181,9 +283,23 @@ hipError_t launch_scatter_residual(const tsa_desc& d, const void* oh, const int3
 
 hipError_t launch_copy_unselected(const tsa_desc& d, const int32_t* inv, const void* res, void* out, hipStream_t s) {
   const int rowb = d.d * (d.dtype == TSA_BF16 ? 2 : 4);
-  const dim3 grid(blocks_for((int64_t)d.L * d.H * (rowb / 16)), d.B);
-  TSA_ROWB_DISPATCH(rowb, scatter_residual_kernel<RB, TSA_BF16, true><<<grid, 256, 0, s>>>(
-                              nullptr, inv, (const char*)res, (char*)out, d.H, heads_per_subset(d), d.L, d.keep));
+  const dim3 grid((unsigned)(((int64_t)d.L * d.H + CU_ROWS - 1) / CU_ROWS), d.B);
+  TSA_ROWB_DISPATCH(rowb, copy_unkept_kernel<RB><<<grid, CU_THREADS, 0, s>>>(
+                              inv, (const char*)res, (char*)out, d.H, heads_per_subset(d), d.L));
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n16 + 255) / 256, 256 * 16);
+  stream_copy_kernel<<<blocks, 256, 0, s>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_counts(const tsa_desc& d, const int32_t* idx, int32_t* counts, hipStream_t s) {
+  const int rows = d.B * subset_rows(d);
+  row_count_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(idx, counts, rows, d.keep);
   return hipGetLastError();
 }
 
