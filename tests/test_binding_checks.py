@@ -59,6 +59,10 @@ def test_helpers_check_index_lists_and_compact_tensors():
         tsa.scatter_residual(oh.float(), idx, r)
     with pytest.raises(ValueError, match="out must have the shape"):
         tsa.scatter_residual(oh, idx, r, out=torch.zeros(B, L - 1, H, d, dtype=bf))
+    with pytest.raises(ValueError, match="idx must be int32"):         # 3 subset rows cannot serve 4 heads
+        tsa.scatter_residual(oh, torch.zeros(B, 3, keep, dtype=torch.int32), r)
+    with pytest.raises(ValueError, match="GPU device"):                # one row per KV head (R = 2) is fine
+        tsa.scatter_residual(oh, torch.zeros(B, Hkv, keep, dtype=torch.int32), r)
     with pytest.raises(ValueError, match="kh, vh"):
         tsa.attn(oh, torch.zeros(B, 3, keep, d, dtype=bf), torch.zeros(B, 3, keep, d, dtype=bf))
     with pytest.raises(ValueError, match="vh must have the shape of kh"):

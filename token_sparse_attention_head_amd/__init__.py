@@ -329,8 +329,12 @@ def _check_qkv(q, k, v=None):
 
 
 def _check_idx(idx, B, heads, kv_heads):
+    """idx int32 [B, R, keep] with R = H or R = Hkv; kv_heads None (not known to the caller):
+    any R dividing H."""
     _tensor(idx, "idx", 3, (torch.int32,))
-    if idx.shape[0] != B or idx.shape[1] not in (heads, kv_heads):
+    R = idx.shape[1]
+    ok = R in (heads, kv_heads) if kv_heads is not None else R >= 1 and heads % R == 0
+    if idx.shape[0] != B or not ok:
         raise ValueError(f"idx must be int32 [B, H, keep] or [B, Hkv, keep] (B={B}, H={heads}, Hkv={kv_heads}); "
                          f"got {tuple(idx.shape)}")
 
@@ -434,8 +438,6 @@ def scatter_residual(oh, idx, residual, out=None):
     B, L, H, d = residual.shape
     _check_idx(idx, B, H, None)
     R = idx.shape[1]
-    if R < 1 or H % R:
-        raise ValueError(f"idx rows must divide the {H} heads; got {tuple(idx.shape)}")
     _tensor(oh, "oh", 4)
     if tuple(oh.shape) != (B, H, idx.shape[2], d) or oh.dtype != residual.dtype:
         raise ValueError(f"oh must be [B, H, keep, d] = {(B, H, idx.shape[2], d)} of the residual's dtype; "
