@@ -65,6 +65,8 @@ extern "C" {
 
 #define TSA_ABI_VERSION 4
 #define TSA_MAX_W 64 /* largest score window the scoring kernel holds in registers */
+/* Scratch bytes tsa_forward_noalloc may use per GPU (its largest workspace). */
+#define TSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum {
   TSA_OK = 0,
@@ -192,6 +194,22 @@ tsa_status tsa_scatter_residual(const tsa_desc* desc, const void* oh, const int3
 tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const void* v,
                        const void* residual, void* out, float* scores_opt, int32_t* idx_opt,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* tsa_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * results as tsa_forward (bit for bit), except that scores and idx are required outputs
+ * and there is no workspace argument: the rest of the workspace (inverse map, select
+ * histograms, score partials; for fp32 also the compact tensors) lives in a static device
+ * array of TSA_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the process
+ * ends.  A problem needing more (tsa_workspace_size(TSA_OP_FORWARD) minus the scores and
+ * idx bytes, rounded up per region) returns TSA_ERR_WORKSPACE before anything runs; 32 MiB
+ * cover a bf16 layer of B = 1, 32 query heads and L up to about 240K, per head.  The first
+ * call on a device looks the array up on the current device (TSA_ERR_LAUNCH if that
+ * fails).  Nothing is allocated or freed, no library routine that allocates is called.
+ * Calls that overlap on one GPU share the array and race: the caller serialises them (one
+ * stream, or events between streams).  Nothing in the array needs to start at zero. */
+tsa_status tsa_forward_noalloc(const tsa_desc* desc, const void* q, const void* k, const void* v,
+                               const void* residual, void* out, float* scores, int32_t* idx, void* stream);
 
 /* Compress, attend and decompress on given subsets (the paper page's Figure 3, stages 1
  * and 2; skill page, Steps 2 and 3): for every query head h with subset r(h) and its

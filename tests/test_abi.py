@@ -11,7 +11,7 @@ tsa = ensure_built()
 L = tsa.lib()
 
 EXPECTED = ["tsa_abi_version", "tsa_attn", "tsa_budget", "tsa_check", "tsa_dense_attn", "tsa_drift",
-            "tsa_forward", "tsa_gather_qkv", "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_sparse_attn",
+            "tsa_forward", "tsa_forward_noalloc", "tsa_gather_qkv", "tsa_scatter_residual", "tsa_score", "tsa_select", "tsa_sparse_attn",
             "tsa_status_str", "tsa_stream_copy", "tsa_workspace_size"]
 
 
@@ -171,6 +171,15 @@ def test_entry_points_reject_before_launch():
     assert call(sa, bd, q, k, v, idx, r, r + 256, ws, big, None) == 7      # partial overlap with the residual
     assert call(sa, bd, q, k, v, idx, r, o, idx + 64, big, None) == 7      # workspace over idx
     assert call(sa, ctypes.byref(D(keep=2)), q, k, v, idx, r, o, ws, big, None) == 3
+    # no workspace argument: scores and idx are required, and a problem whose workspace
+    # exceeds the static scratch array is rejected before anything runs
+    na = "tsa_forward_noalloc"
+    assert call(na, bd, q, k, v, r, o, None, idx, None) == 1
+    assert call(na, bd, q, k, v, r, o, sc, None, None) == 1
+    assert call(na, bd, q, k, v, r, o, sc + 4, idx, None) == 5
+    assert call(na, ctypes.byref(D(keep=2)), q, k, v, r, o, sc, idx, None) == 3
+    assert call(na, ctypes.byref(D(L=262144, keep=4096)), q, k, v, r, o, sc, idx, None) == 6   # inverse map 33.5 MB
+    assert call(na, ctypes.byref(D(L=0, keep=0)), None, None, None, None, None, None, None, None) == 0
     # plain copy
     assert call("tsa_stream_copy", o, None, 4096, None) == 1
     assert call("tsa_stream_copy", o, q, 4095, None) == 5

@@ -73,6 +73,7 @@ _SIGS = {
     "tsa_drift": ([_DP, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_sparse_attn": ([_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "tsa_stream_copy": ([_P, _P, _SZ, _P], ctypes.c_int),
+    "tsa_forward_noalloc": ([_DP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -247,6 +248,14 @@ def tsa_forward(desc, q, k, v, residual, out, scores=None, idx=None, ws=None, ws
     _call("tsa_forward", ctypes.byref(desc), _arg(q, desc, "full", "q"), _arg(k, desc, "kv", "k"),
           _arg(v, desc, "kv", "v"), _arg(residual, desc, "full", "residual"), _arg(out, desc, "full", "out"),
           _arg(scores, desc, "scores", "scores", torch.float32), _arg(idx, desc, "idx", "idx", torch.int32), w, n,
+          _stream(stream))
+
+
+def tsa_forward_noalloc(desc, q, k, v, residual, out, scores, idx, stream=None):
+    """tsa_forward on the library's static per-GPU scratch (no workspace; scores and idx required)."""
+    _call("tsa_forward_noalloc", ctypes.byref(desc), _arg(q, desc, "full", "q"), _arg(k, desc, "kv", "k"),
+          _arg(v, desc, "kv", "v"), _arg(residual, desc, "full", "residual"), _arg(out, desc, "full", "out"),
+          _arg(scores, desc, "scores", "scores", torch.float32), _arg(idx, desc, "idx", "idx", torch.int32),
           _stream(stream))
 
 

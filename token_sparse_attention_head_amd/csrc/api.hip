@@ -4,9 +4,13 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
+
+// The scratch array of tsa_forward_noalloc (see device_scratch below).
+static __device__ __align__(256) char scratch[TSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -129,14 +133,15 @@ struct FwdLayout {
   size_t scores, idx, inv, sel, part, stat, counts, plan, qh, kh, vh, oh, total;
 };
 
-FwdLayout fwd_layout(const tsa_desc& d) {
+// hold_outputs = false leaves out the scores and idx regions (the caller passes both).
+FwdLayout fwd_layout(const tsa_desc& d, bool hold_outputs = true) {
   const Sizes z = sizes_of(d);
   const size_t comp = fused_forward(d) ? 0 : round_up(z.compact);
   const size_t kvc = fused_forward(d) ? 0 : round_up(z.kvc);
   FwdLayout f;
   size_t o = 0;
-  f.scores = o; o += round_up(z.scores);
-  f.idx = o; o += round_up(z.idx);
+  f.scores = o; o += hold_outputs ? round_up(z.scores) : 0;
+  f.idx = o; o += hold_outputs ? round_up(z.idx) : 0;
   f.inv = o; o += round_up(z.inv);
   f.sel = o; o += round_up(z.sel);
   f.part = o; o += round_up(z.part);
@@ -177,6 +182,80 @@ SparseLayout sparse_layout(const tsa_desc& d) {
 template <typename P>
 P* at(void* base, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+// Pointer and alignment checks of the forward's tensors (scores / idx may be NULL).
+tsa_status forward_args(const void* q, const void* k, const void* v, const void* residual, const void* out,
+                        const float* scores, const int32_t* idx) {
+  if (!q || !k || !v || !residual || !out) return TSA_ERR_NULL;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(residual) || !aligned(out) || !aligned(scores) ||
+      !aligned(idx))
+    return TSA_ERR_ALIGN;
+  return TSA_OK;
+}
+
+// The forward on a workspace laid out by f: overlap checks, then the stages on stream s.
+// scores_opt / idx_opt NULL: they live in the workspace (f holds their regions).
+tsa_status forward_run(const tsa_desc& d, const void* q, const void* k, const void* v, const void* residual,
+                       void* out, float* scores_opt, int32_t* idx_opt, void* ws, const FwdLayout& f, hipStream_t s) {
+  const Sizes z = sizes_of(d);
+  const Range ro{out, z.q}, rw{ws, f.total}, rs{scores_opt, z.scores}, ri{idx_opt, z.idx};
+  const Range ins[4] = {{q, z.q}, {k, z.kv}, {v, z.kv}, {residual, z.q}};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(rw, ins[i]) || overlap(rs, ins[i]) || overlap(ri, ins[i])) return TSA_ERR_ALIAS;
+    if (i < 3 && overlap(ro, ins[i])) return TSA_ERR_ALIAS;
+  }
+  if (out != residual && overlap(ro, ins[3])) return TSA_ERR_ALIAS;
+  if (overlap(ro, rw) || overlap(ro, rs) || overlap(ro, ri) || overlap(rs, rw) || overlap(ri, rw) || overlap(rs, ri))
+    return TSA_ERR_ALIAS;
+
+  float* scores = scores_opt ? scores_opt : at<float>(ws, f.scores);
+  int32_t* idx = idx_opt ? idx_opt : at<int32_t>(ws, f.idx);
+  int32_t* inv = at<int32_t>(ws, f.inv);
+  void* qh = at<char>(ws, f.qh);
+  void* kh = at<char>(ws, f.kh);
+  void* vh = at<char>(ws, f.vh);
+  void* oh = at<char>(ws, f.oh);
+  const bool in_place = out == residual;
+  TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
+  int32_t* counts = d.tau > 0.f ? at<int32_t>(ws, f.counts) : nullptr;
+  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, counts, at<char>(ws, f.sel), s), s));
+  if (fused_forward(d)) {
+    // Rows a head does not keep are the residual (copied out of place, untouched in place);
+    // the attention epilogue writes residual + O into the kept rows.
+    if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
+    if (d.keep == 0) return TSA_OK;
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, f.plan), residual, out, s), s);
+  }
+  if (d.keep > 0) {
+    TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));
+    TSA_TRY(after_launch(launch_attn_compact(d, qh, kh, vh, oh, s), s));
+  }
+  if (in_place) return after_launch(tsa::launch_scatter_inplace(d, oh, idx, out, s), s);
+  return after_launch(tsa::launch_scatter_residual(d, oh, inv, residual, out, s), s);
+}
+
+// Scratch of tsa_forward_noalloc: a device array in the library's code object, one copy per
+// GPU, held until the process ends.  Host code never uses the array's name as an address:
+// the first call on each device (with that device current) looks the device address up
+// with hipGetSymbolAddress and keeps it; every later use goes through that address.  No
+// region of it has to start at zero: every kernel of the forward writes what it later reads
+// (the select clears its own histograms).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+tsa_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TSA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TSA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
 }
 
 }  // namespace
@@ -336,48 +415,25 @@ tsa_status tsa_forward(const tsa_desc* desc, const void* q, const void* k, const
   TSA_TRY(check_full(desc));
   const tsa_desc& d = *desc;
   if (empty_problem(d)) return TSA_OK;
-  if (!q || !k || !v || !residual || !out) return TSA_ERR_NULL;
-  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(residual) || !aligned(out) || !aligned(scores_opt) ||
-      !aligned(idx_opt) || !aligned(ws))
-    return TSA_ERR_ALIGN;
-  const Sizes z = sizes_of(d);
+  TSA_TRY(forward_args(q, k, v, residual, out, scores_opt, idx_opt));
+  if (!aligned(ws)) return TSA_ERR_ALIGN;
   const FwdLayout f = fwd_layout(d);
   if (!ws || ws_bytes < f.total) return TSA_ERR_WORKSPACE;
-  const Range ro{out, z.q}, rw{ws, f.total}, rs{scores_opt, z.scores}, ri{idx_opt, z.idx};
-  const Range ins[4] = {{q, z.q}, {k, z.kv}, {v, z.kv}, {residual, z.q}};
-  for (int i = 0; i < 4; ++i) {
-    if (overlap(rw, ins[i]) || overlap(rs, ins[i]) || overlap(ri, ins[i])) return TSA_ERR_ALIAS;
-    if (i < 3 && overlap(ro, ins[i])) return TSA_ERR_ALIAS;
-  }
-  if (out != residual && overlap(ro, ins[3])) return TSA_ERR_ALIAS;
-  if (overlap(ro, rw) || overlap(ro, rs) || overlap(ro, ri) || overlap(rs, rw) || overlap(ri, rw) || overlap(rs, ri))
-    return TSA_ERR_ALIAS;
+  return forward_run(d, q, k, v, residual, out, scores_opt, idx_opt, ws, f, static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* scores = scores_opt ? scores_opt : at<float>(ws, f.scores);
-  int32_t* idx = idx_opt ? idx_opt : at<int32_t>(ws, f.idx);
-  int32_t* inv = at<int32_t>(ws, f.inv);
-  void* qh = at<char>(ws, f.qh);
-  void* kh = at<char>(ws, f.kh);
-  void* vh = at<char>(ws, f.vh);
-  void* oh = at<char>(ws, f.oh);
-  const bool in_place = out == residual;
-  TSA_TRY(after_launch(tsa::launch_score(d, q, k, scores, at<float2>(ws, f.part), at<float2>(ws, f.stat), s), s));
-  int32_t* counts = d.tau > 0.f ? at<int32_t>(ws, f.counts) : nullptr;
-  TSA_TRY(after_launch(tsa::launch_select(d, scores, idx, in_place ? nullptr : inv, counts, at<char>(ws, f.sel), s), s));
-  if (fused_forward(d)) {
-    // Rows a head does not keep are the residual (copied out of place, untouched in place);
-    // the attention epilogue writes residual + O into the kept rows.
-    if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
-    if (d.keep == 0) return TSA_OK;
-    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, f.plan), residual, out, s), s);
-  }
-  if (d.keep > 0) {
-    TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));
-    TSA_TRY(after_launch(launch_attn_compact(d, qh, kh, vh, oh, s), s));
-  }
-  if (in_place) return after_launch(tsa::launch_scatter_inplace(d, oh, idx, out, s), s);
-  return after_launch(tsa::launch_scatter_residual(d, oh, inv, residual, out, s), s);
+tsa_status tsa_forward_noalloc(const tsa_desc* desc, const void* q, const void* k, const void* v,
+                               const void* residual, void* out, float* scores, int32_t* idx, void* stream) {
+  TSA_TRY(check_full(desc));
+  const tsa_desc& d = *desc;
+  if (empty_problem(d)) return TSA_OK;
+  if (!scores || !idx) return TSA_ERR_NULL;
+  TSA_TRY(forward_args(q, k, v, residual, out, scores, idx));
+  const FwdLayout f = fwd_layout(d, false);
+  if (f.total > TSA_NOALLOC_SCRATCH_BYTES) return TSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  TSA_TRY(device_scratch(&ws));
+  return forward_run(d, q, k, v, residual, out, scores, idx, ws, f, static_cast<hipStream_t>(stream));
 }
 
 tsa_status tsa_sparse_attn(const tsa_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
