@@ -10,19 +10,19 @@
 //   s[b,h,j] = sum_{i in [L-W', L), i >= j} exp(z_ij - m_i) / l_i,
 //   z_ij = scale <q_i, k_j>,  m_i = max_{j<=i} z_ij,  l_i = sum_{j<=i} exp(z_ij - m_i).
 //
-// Pass 1 (one wave per (b, h, key chunk)): z on MFMA with keys as rows and window
-// queries as columns, so each lane owns one query and a running (max, sum) over its
-// keys.  A merge kernel folds the chunks into (m_i, 1/l_i).  Pass 2 recomputes z with
-// window queries as rows and keys as columns, so each lane owns one key and sums its
-// probabilities over the window rows in a fixed order (the same order for every key,
-// so equal inputs give bit-equal scores).  Probabilities and sums stay fp32.
+// Pass 1 computes z with keys as rows and window queries as columns, so each lane owns a
+// query and a running sum of exp2 over its keys against a reference; a merge kernel folds the
+// key chunks into (m_i, 1/l_i).  Pass 2 recomputes z with window queries as rows and keys as
+// columns, so each lane owns one key and sums its probabilities over the window rows in a
+// fixed order (the same order for every key, so equal inputs give bit-equal scores).
+// Probabilities and sums stay fp32.
 //
-// bf16: a workgroup is four query heads of one KV group (one wave each) on one key
-// chunk.  64-key tiles of the shared K rows are loaded once per workgroup (each lane a few
-// 16-byte chunks, two tiles in flight in registers) into padded LDS rows, and every wave
-// reads its MFMA operands from there, so the K bytes cross HBM once and enough of them are
-// in flight to hide its latency.  fp32: every wave reads its operands straight from global
-// memory (a lane reads one contiguous half of a head-dim row).
+// bf16: a workgroup is four query heads of one KV group (one wave each) on one key chunk,
+// on the 16x16x32 MFMA (details at the kernels).  64-key tiles of the shared K rows are
+// loaded once per workgroup into padded LDS rows that all four waves read their operands
+// from, so the K bytes cross HBM once.  fp32: every wave reads its operands straight from
+// global memory (a lane reads one contiguous half of a head-dim row) on the 32x32x2 fp32
+// MFMA, with an exact running max in pass 1.
 #include <type_traits>
 
 #include "common.h"
@@ -231,17 +231,17 @@ __global__ __launch_bounds__(256) void score_pass2_kernel(const T* __restrict__ 
 constexpr int SBN = 64;       // keys per staged tile
 constexpr int SPF = 2;        // tiles in flight in registers
 
-// Cooperative staging of 64-key K tiles of one (b, KV head) into padded LDS rows
-// (2D + 16 bytes apart: the 16-byte operand reads of 16 consecutive keys hit every bank once).
-template <int D>
+// Cooperative staging of 64-key K tiles of one (b, KV head) into padded LDS rows KP_ bytes
+// apart, NSETS tiles in flight in registers.
+template <int D, int KP_, int NSETS = SPF>
 struct KStage {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int LPT = SBN * CPR / 256;        // chunks per thread per tile
-  static constexpr int KP = 2 * D + 16;
+  static constexpr int KP = KP_;
   const char* base;          // K row of position 0 for this (b, KV head), bytes
   int64_t row_bytes;         // bytes between positions
   int L, lrow[LPT], lch[LPT], soff[LPT];
-  u32x4 st[SPF][LPT];
+  u32x4 st[NSETS][LPT];
   __device__ __forceinline__ void init(const __bf16* k, const ScoreGeom& g, int b, int kvh) {
     base = reinterpret_cast<const char*>(k + ((int64_t)b * g.L * g.Hkv + kvh) * D);
     row_bytes = (int64_t)g.Hkv * D * 2;
@@ -266,139 +266,245 @@ struct KStage {
   }
 };
 
-// The K operand of one 32-key block for this lane (key kb * 32 + lane % 32, d half lane / 32).
-template <int D>
-__device__ __forceinline__ void lds_key(const char* tile, int kb, int lane, HalfRow<__bf16, D>& kf) {
-  const char* a = tile + (kb * 32 + (lane & 31)) * KStage<D>::KP + (lane >> 5) * D;
-#pragma unroll
-  for (int s2 = 0; s2 < D / 16; ++s2) kf.f[s2] = *reinterpret_cast<const bf16x8*>(a + s2 * 16);
-}
-
-// Workgroup unit -> (b, KV head, head quad, chunk); wave w takes query head kvh*G + 4*quad + w.
+// Consecutive workgroups take the head quads and KV heads of one key chunk, so the
+// workgroups in flight read whole K rows of consecutive positions together (a position's
+// KV heads are adjacent in memory; one head's rows alone are a 2 D-byte piece of every
+// Hkv * 2 D bytes).
 __device__ __forceinline__ void unit_of4(const ScoreGeom& g, int& b, int& kvh, int& quad, int& ch) {
   const int nq = (g.G + 3) / 4;
   int u = blockIdx.x;
-  ch = u % g.nchunk;
-  u /= g.nchunk;
   quad = u % nq;
   u /= nq;
   kvh = u % g.Hkv;
-  b = u / g.Hkv;
+  u /= g.Hkv;
+  ch = u % g.nchunk;
+  b = u / g.nchunk;
 }
 
-template <int D, int RB>
-__global__ __launch_bounds__(256) void score_pass1_lds_kernel(const __bf16* __restrict__ q,
-                                                              const __bf16* __restrict__ k,
-                                                              float2* __restrict__ part, ScoreGeom g, float c) {
-  __shared__ __attribute__((aligned(16))) char lds[2][SBN * KStage<D>::KP];
-  const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
-  const int hf = lane >> 5;
-  int b, kvh, quad, ch;
-  unit_of4(g, b, kvh, quad, ch);
-  const int hg = 4 * quad + wave;                    // head within the group
-  const bool active = hg < g.G;
-  const int h = kvh * g.G + (active ? hg : 0);
-  HalfRow<__bf16, D> qf[RB];
-  load_window_q<__bf16, D, RB>(q, g, b, h, lane, qf);
-  float m[RB], sacc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) { m[rb] = NEG_BIG; sacc[rb] = 0.f; }
+// ---- bf16 kernels on the 16x16x32 MFMA ------------------------------------------------
+//
+// v_mfma_f32_16x16x32_bf16: operand lanes l supply row (or column) l % 16 and the
+// contraction slice 8 (l / 16) .. +7 of each 32-wide step; the 16x16 result gives lane l
+// column l % 16 and rows 4 (l / 16) + i, i = 0..3.  The window rows form RB blocks of 16
+// (block qb, row r = window row 16 qb + r).  A lane's Q fragment of block qb and step s is
+// row 16 qb + l % 16 at d = 32 s + 8 (l / 16); its K fragment of a 16-key block is key
+// l % 16 at the same d, read from LDS rows 2D + 32 bytes apart (the four lane groups of a
+// key read its 64 contiguous bytes of the step, and the 16 keys fall on distinct banks).
+// Every K fragment feeds RB independent products (one per query block), so no product
+// waits for the one before it.
+//
+// Pass 1 forms S^T = K Q^T (lane: one query of each block, four keys of each 16-key block)
+// and keeps, per lane and query, a sum of exp2 against a lazily moved reference m: the
+// block's probabilities are taken against m as it is and their sum (below 2^32: nothing near
+// overflow) decides whether that was safe; only otherwise (the first block, or a jump of the
+// logits by 32 in log2 units) the lane's max moves m and rescales the sum.  The four lanes of
+// a query are merged at the end (max, then the rescaled sums), so no row max is taken per
+// element.  Pass 2 forms S = Q K^T (lane: one key, four queries of each block) and sums the
+// normalised probabilities of its key over its 4 RB queries in a fixed order, then over the
+// four lane groups (xor 16, then xor 32): the same order for every key.
 
-  const int j_beg = ch * g.chunk;
-  const int j_end = min(g.L, j_beg + g.chunk);
-  const int nt = (j_end - j_beg + SBN - 1) / SBN;
-  const int first_row_pos = g.L - g.Wp;
-  KStage<D> ks;
-  ks.init(k, g, b, kvh);
-  ks.load(0, j_beg);
-  ks.load(1, j_beg + SBN);
-  auto step = [&](int t, char* tile, int set) __attribute__((always_inline)) {
-    ks.store(set, tile);
-    __syncthreads();
-    ks.load(set, j_beg + (t + SPF) * SBN);
-    const int j0t = j_beg + t * SBN;
-    if (!active || t >= nt) return;
+constexpr int KP16_PAD = 32;
+constexpr int SPF16 = 2;      // K tiles in flight in registers
+
+template <int D, int RB>
+__device__ __forceinline__ void load_window_q16(const __bf16* q, const ScoreGeom& g, int b, int h, int lane,
+                                                bf16x8 (&qf)[RB][D / 32]) {
+  const int lq = lane & 15, gq = lane >> 4;
 #pragma unroll
-    for (int kb = 0; kb < SBN / 32; ++kb) {
-      // Chunks are whole tiles except the last, which ends at L: keys at or past L come
-      // after every window row, so the causal mask also removes the ragged tail.
-      const int j0 = j0t + kb * 32;
-      __builtin_amdgcn_sched_barrier(0);
-      HalfRow<__bf16, D> kf;
-      lds_key<D>(tile, kb, lane, kf);
-      // The causal mask only touches the blocks that reach the window rows: those take a
-      // separate copy of the code so the others run without per-element selects.
-      auto rows = [&](auto mask_tag) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+  for (int qb = 0; qb < RB; ++qb) {
+    const int row = 16 * qb + lq;
+    if (row < g.Wp) {
+      const __bf16* src = q + ((int64_t)b * g.L + g.L - g.Wp + row) * g.q_row + (int64_t)h * D + 8 * gq;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x16 acc = {};
-          acc = dot_tile<__bf16, D>(acc, kf, qf[rb]);   // rows: keys, columns: window queries
-          const int i = first_row_pos + rb * 32 + (lane & 31);
-          float tmax = -__builtin_huge_valf();
+      for (int st = 0; st < D / 32; ++st) qf[qb][st] = *reinterpret_cast<const bf16x8*>(src + 32 * st);
+    } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (MASK && j0 + acc_row(r, hf) > i) acc[r] = -__builtin_huge_valf();
-            tmax = fmaxf(tmax, acc[r]);
-          }
-          const float mn = fmaxf(m[rb], tmax * c);
-          float add = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mn));
-          sacc[rb] = sacc[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + add;
-          m[rb] = mn;
-        }
-      };
-      if (j0 + 31 > first_row_pos) rows(std::true_type{});
-      else rows(std::false_type{});
+      for (int st = 0; st < D / 32; ++st) qf[qb][st] = bf16x8{};
     }
-  };
-  for (int t = 0; t < nt; t += 2) {
-    step(t, lds[0], 0);
-    step(t + 1, lds[1], 1);
   }
-  if (!active) return;
+}
+
+__device__ __forceinline__ f32x4 mfma16s(f32x4 c, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Both passes are software-pipelined over 16-key blocks: the products of block kb are
+// issued interleaved with the softmax arithmetic of block kb - 1 (one matrix instruction,
+// then three vector instructions, as scheduling groups), so a wave keeps the matrix cores
+// and its vector unit busy at once.  The causal mask is evaluated only in steps whose
+// blocks reach the window rows (a step processes block 3 of the previous tile and blocks
+// 0-2 of its own).
+
+// Sixteen groups of one matrix instruction followed by three vector instructions.
+__device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float mo = xor32(m[rb]);
-    const float so = xor32(sacc[rb]);
-    const float M = fmaxf(m[rb], mo);
-    const float S = sacc[rb] * __builtin_amdgcn_exp2f(m[rb] - M) + so * __builtin_amdgcn_exp2f(mo - M);
-    const int row = rb * 32 + (lane & 31);
-    if (hf == 0 && row < g.Wp)
-      part[(((int64_t)b * g.H + h) * g.nchunk + ch) * g.Wp + row] = make_float2(M, S);
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);   // vector ALU, transcendental included
   }
 }
 
 template <int D, int RB>
-__global__ __launch_bounds__(256, 2) void score_pass2_lds_kernel(const __bf16* __restrict__ q,
-                                                              const __bf16* __restrict__ k,
-                                                              const float2* __restrict__ stat,
-                                                              float* __restrict__ scores, ScoreGeom g, float c) {
-  __shared__ __attribute__((aligned(16))) char lds[2][SBN * KStage<D>::KP];
+__global__ __launch_bounds__(256, 2) void score_pass1_k16_kernel(const __bf16* __restrict__ q,
+                                                                 const __bf16* __restrict__ k,
+                                                                 float2* __restrict__ part, ScoreGeom g, float c) {
+  constexpr int ST = D / 32, KP = 2 * D + KP16_PAD, NS = SPF16;
+  __shared__ __attribute__((aligned(16))) char lds[2][SBN * KP];
   const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
-  const int hf = lane >> 5;
+  const int lq = lane & 15, gq = lane >> 4;
   int b, kvh, quad, ch;
   unit_of4(g, b, kvh, quad, ch);
   const int hg = 4 * quad + wave;
   const bool active = hg < g.G;
   const int h = kvh * g.G + (active ? hg : 0);
-  HalfRow<__bf16, D> qf[RB];
-  load_window_q<__bf16, D, RB>(q, g, b, h, lane, qf);
-  float mrow[RB][16], il[RB][16];
-  const float2* st = stat + ((int64_t)b * g.H + h) * g.Wp;
+  bf16x8 qf[RB][ST];
+  load_window_q16<D, RB>(q, g, b, h, lane, qf);
+  float m[RB], l[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int qb = 0; qb < RB; ++qb) { m[qb] = NEG_BIG; l[qb] = 0.f; }
+
+  const int j_beg = ch * g.chunk;
+  const int j_end = min(g.L, j_beg + g.chunk);
+  const int nt = (j_end - j_beg + SBN - 1) / SBN;
+  const int first_row_pos = g.L - g.Wp;
+  const int koff = lq * KP + 16 * gq;
+  // The block in flight: its products (keys jp + 4 gq + i, query 16 qb + lq).  Before the
+  // first block it holds -inf everywhere, which adds nothing.
+  f32x4 pacc[RB];
+  int jp = j_beg;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rb * 32 + acc_row(r, hf);
+  for (int qb = 0; qb < RB; ++qb) pacc[qb] = f32x4{-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf()};
+
+  // Softmax sums of the block in pacc (keys from jp) into ls; MASK applies the causal mask.
+  float ls[RB];
+  auto softmax_prev = [&](auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (MASK) {
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (jp + 4 * gq + i > first_row_pos + 16 * qb + lq) pacc[qb][i] = -__builtin_huge_valf();
+    }
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(pacc[qb][0], c, -m[qb]));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(pacc[qb][1], c, -m[qb]));
+      const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(pacc[qb][2], c, -m[qb]));
+      const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(pacc[qb][3], c, -m[qb]));
+      ls[qb] = (e0 + e1) + (e2 + e3);
+    }
+  };
+  // Guard of those sums (after the next block's products are issued): a sum of 2^32 or more
+  // (or the first block, against the initial reference) moves the reference to the lane's
+  // max and the sums are taken again; then they join the running sums.
+  auto guard_prev = [&]() __attribute__((always_inline)) {
+    bool unsafe = false;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) unsafe |= !(ls[qb] < 4294967296.0f);
+    if (__ballot(unsafe) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) {
+        const float tmax = fmaxf(fmaxf(pacc[qb][0], pacc[qb][1]), fmaxf(pacc[qb][2], pacc[qb][3]));
+        const float mn = fmaxf(m[qb], tmax * c);   // m stays finite (starts at NEG_BIG)
+        l[qb] *= __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+      }
+      softmax_prev(std::false_type{});   // pacc is already masked
+    }
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) l[qb] += ls[qb];
+  };
+
+  KStage<D, KP, NS> ks;
+  ks.init(k, g, b, kvh);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) ks.load(i, j_beg + i * SBN);
+  auto step = [&](int t, char* tile, int set) __attribute__((always_inline)) {
+    ks.store(set, tile);
+    __syncthreads();
+    ks.load(set, j_beg + (t + NS) * SBN);
+    if (!active || t >= nt) return;
+    const int j0t = j_beg + t * SBN;
+    auto blocks = [&](auto mask_tag) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < SBN / 16; ++kb) {
+        bf16x8 kf[ST];
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+          kf[st] = *reinterpret_cast<const bf16x8*>(tile + 16 * kb * KP + koff + 64 * st);
+        f32x4 acc[RB];
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) acc[qb] = f32x4{};
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+#pragma unroll
+          for (int qb = 0; qb < RB; ++qb) acc[qb] = mfma16s(acc[qb], kf[st], qf[qb][st]);   // rows: keys, cols: queries
+        softmax_prev(mask_tag);
+        interleave_mfma_valu();
+        guard_prev();
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) pacc[qb] = acc[qb];
+        jp = j0t + 16 * kb;
+      }
+    };
+    if (j0t + SBN - 17 > first_row_pos) blocks(std::true_type{});
+    else blocks(std::false_type{});
+  };
+  for (int t = 0; t < nt; t += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(t + u, lds[u & 1], u);
+  }
+  if (!active) return;
+  softmax_prev(std::true_type{});    // the last block
+  guard_prev();
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) {
+    float M = m[qb], S = l[qb];
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {     // merge the four lanes of the query
+      const float mo = __shfl_xor(M, x, TSA_WAVE);
+      const float so = __shfl_xor(S, x, TSA_WAVE);
+      const float mm = fmaxf(M, mo);
+      S = S * __builtin_amdgcn_exp2f(M - mm) + so * __builtin_amdgcn_exp2f(mo - mm);
+      M = mm;
+    }
+    const int row = 16 * qb + lq;
+    if (gq == 0 && row < g.Wp) part[(((int64_t)b * g.H + h) * g.nchunk + ch) * g.Wp + row] = make_float2(M, S);
+  }
+}
+
+template <int D, int RB>
+__global__ __launch_bounds__(256, 2) void score_pass2_k16_kernel(const __bf16* __restrict__ q,
+                                                                 const __bf16* __restrict__ k,
+                                                                 const float2* __restrict__ stat,
+                                                                 float* __restrict__ scores, ScoreGeom g, float c) {
+  constexpr int ST = D / 32, KP = 2 * D + KP16_PAD, NS = 2;
+  __shared__ __attribute__((aligned(16))) char lds[2][SBN * KP];
+  const int lane = lane_id(), wave = threadIdx.x / TSA_WAVE;
+  const int lq = lane & 15, gq = lane >> 4;
+  int b, kvh, quad, ch;
+  unit_of4(g, b, kvh, quad, ch);
+  const int hg = 4 * quad + wave;
+  const bool active = hg < g.G;
+  const int h = kvh * g.G + (active ? hg : 0);
+  bf16x8 qf[RB][ST];
+  load_window_q16<D, RB>(q, g, b, h, lane, qf);
+  // Statistics of the four window rows this lane holds in each block (rows 16 qb + 4 gq + i).
+  float mrow[RB][4], il[RB][4];
+  const float2* stp = stat + ((int64_t)b * g.H + h) * g.Wp;
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * qb + 4 * gq + i;
       if (row < g.Wp) {
-        const float2 v = st[row];
-        mrow[rb][r] = v.x;
-        il[rb][r] = v.y;
+        const float2 v = stp[row];
+        mrow[qb][i] = v.x;
+        il[qb][i] = v.y;
       } else {
-        mrow[rb][r] = __builtin_huge_valf();   // exp2(z - inf) = 0
-        il[rb][r] = 0.f;
+        mrow[qb][i] = __builtin_huge_valf();   // exp2(z - inf) = 0
+        il[qb][i] = 0.f;
       }
     }
 
@@ -406,50 +512,78 @@ __global__ __launch_bounds__(256, 2) void score_pass2_lds_kernel(const __bf16* _
   const int j_end = min(g.L, j_beg + g.chunk);
   const int nt = (j_end - j_beg + SBN - 1) / SBN;
   const int first_row_pos = g.L - g.Wp;
+  const int koff = lq * KP + 16 * gq;
   float* out = scores + ((int64_t)b * g.H + h) * g.L;
-  KStage<D> ks;
+  // The block in flight (key jp + lq, queries 16 qb + 4 gq + i); before the first block it
+  // holds zeros for a key at j_end, which is not written.
+  f32x4 pacc[RB];
+  int jp = j_end;
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) pacc[qb] = f32x4{};
+
+  // Column sum of the key this lane holds in the block in pacc, over its 4 RB queries in a
+  // fixed order, then over the four lane groups; returns the write of the result.
+  auto colsum_prev = [&](auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int j = jp + lq;
+    float col = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pacc[qb][i], c, -mrow[qb][i])) * il[qb][i];
+        if (MASK && j > first_row_pos + 16 * qb + 4 * gq + i) p = 0.f;
+        col += p;
+      }
+    return [=]() __attribute__((always_inline)) {
+      float cs = col;
+      cs += __shfl_xor(cs, 16, TSA_WAVE);
+      cs += __shfl_xor(cs, 32, TSA_WAVE);
+      if (gq == 0 && j < j_end) out[j] = cs;
+    };
+  };
+
+  KStage<D, KP, NS> ks;
   ks.init(k, g, b, kvh);
-  ks.load(0, j_beg);
-  ks.load(1, j_beg + SBN);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) ks.load(i, j_beg + i * SBN);
   auto step = [&](int t, char* tile, int set) __attribute__((always_inline)) {
     ks.store(set, tile);
     __syncthreads();
-    ks.load(set, j_beg + (t + SPF) * SBN);
-    const int j0t = j_beg + t * SBN;
+    ks.load(set, j_beg + (t + NS) * SBN);
     if (!active || t >= nt) return;
+    const int j0t = j_beg + t * SBN;
+    auto blocks = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < SBN / 32; ++kb) {
-      const int j0 = j0t + kb * 32;
-      __builtin_amdgcn_sched_barrier(0);
-      HalfRow<__bf16, D> kf;
-      lds_key<D>(tile, kb, lane, kf);
-      const int j = j0 + (lane & 31);
-      auto cols = [&](auto mask_tag) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        float col = 0.f;
+      for (int kb = 0; kb < SBN / 16; ++kb) {
+        bf16x8 kf[ST];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x16 acc = {};
-          acc = dot_tile<__bf16, D>(acc, qf[rb], kf);   // rows: window queries, columns: keys
+        for (int st = 0; st < ST; ++st)
+          kf[st] = *reinterpret_cast<const bf16x8*>(tile + 16 * kb * KP + koff + 64 * st);
+        f32x4 acc[RB];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], c, -mrow[rb][r])) * il[rb][r];
-            if (MASK && j > first_row_pos + rb * 32 + acc_row(r, hf)) p = 0.f;
-            col += p;
-          }
-        }
-        return col;
-      };
-      float col = j0 + 31 > first_row_pos ? cols(std::true_type{}) : cols(std::false_type{});
-      col += xor32(col);
-      if (hf == 0 && j < j_end) out[j] = col;
-    }
-    __builtin_amdgcn_sched_barrier(0);
+        for (int qb = 0; qb < RB; ++qb) acc[qb] = f32x4{};
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+#pragma unroll
+          for (int qb = 0; qb < RB; ++qb) acc[qb] = mfma16s(acc[qb], qf[qb][st], kf[st]);   // rows: queries, cols: keys
+        auto finish = colsum_prev(mask_tag);
+        interleave_mfma_valu();
+        finish();
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) pacc[qb] = acc[qb];
+        jp = j0t + 16 * kb;
+      }
+    };
+    if (j0t + SBN - 17 > first_row_pos) blocks(std::true_type{});
+    else blocks(std::false_type{});
   };
-  for (int t = 0; t < nt; t += 2) {
-    step(t, lds[0], 0);
-    step(t + 1, lds[1], 1);
+  for (int t = 0; t < nt; t += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(t + u, lds[u & 1], u);
   }
+  if (!active) return;
+  colsum_prev(std::true_type{})();    // the last block
 }
 
 template <typename T, int D>
@@ -465,15 +599,22 @@ hipError_t launch_score_t(const tsa_desc& d, const void* q, const void* k, float
   const float c = scale * TSA_LOG2E;
   if constexpr (sizeof(T) == 2) {
     const unsigned blocks = (unsigned)(d.B * d.Hkv * ((g.G + 3) / 4) * g.nchunk);
-    if (g.Wp > 32)
-      score_pass1_lds_kernel<D, 2><<<blocks, 256, 0, s>>>((const __bf16*)q, (const __bf16*)k, part, g, c);
-    else
-      score_pass1_lds_kernel<D, 1><<<blocks, 256, 0, s>>>((const __bf16*)q, (const __bf16*)k, part, g, c);
+    const __bf16* qb = static_cast<const __bf16*>(q);
+    const __bf16* kb = static_cast<const __bf16*>(k);
+    // RB = 16-row blocks of window queries (W' <= 64).
+    switch ((g.Wp + 15) / 16) {
+      case 1: score_pass1_k16_kernel<D, 1><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
+      case 2: score_pass1_k16_kernel<D, 2><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
+      case 3: score_pass1_k16_kernel<D, 3><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
+      default: score_pass1_k16_kernel<D, 4><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
+    }
     score_merge_kernel<<<d.B * d.H, 64 * MERGE_PARTS, 0, s>>>(part, stat, g.nchunk, g.Wp);
-    if (g.Wp > 32)
-      score_pass2_lds_kernel<D, 2><<<blocks, 256, 0, s>>>((const __bf16*)q, (const __bf16*)k, stat, scores, g, c);
-    else
-      score_pass2_lds_kernel<D, 1><<<blocks, 256, 0, s>>>((const __bf16*)q, (const __bf16*)k, stat, scores, g, c);
+    switch ((g.Wp + 15) / 16) {
+      case 1: score_pass2_k16_kernel<D, 1><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
+      case 2: score_pass2_k16_kernel<D, 2><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
+      case 3: score_pass2_k16_kernel<D, 3><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
+      default: score_pass2_k16_kernel<D, 4><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
+    }
     return hipGetLastError();
   }
   const int units = d.B * d.H * g.nchunk;
