@@ -42,6 +42,8 @@
 //   With adaptive budgets (rows differ per head) attn_plan_kernel first deals the heads,
 //   sorted by attention work, to the XCDs in snake order, keeping that locality while
 //   the XCDs get equal work.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -69,6 +71,7 @@ struct AttnParams {
   const int32_t* plan;     // with counts: the per-XCD head lists of attn_plan_kernel, or NULL
   int plan_cap;            // heads per XCD list in the plan
   int L;                   // fused forward: sequence length (index-list entries are clamped below it)
+  int interleave;          // 1: an XCD deals the tiles of its heads in turn (longest first over all of them)
 };
 
 // Plan of the fused attention under adaptive budgets (rows differ per head).  A head's
@@ -495,10 +498,19 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
       tile = (n + BM - 1) / BM - 1 - r;
       if (tile < 0) return;
     } else if (p.BH % 8 == 0) {
+      // Heads are dealt to XCDs in blocks of BH / 8.  Long rows: one head at a time per XCD,
+      // so its workgroups share the head's K/V tiles in that XCD's L2.  Few tiles per head:
+      // the tiles of the XCD's heads in turn, longest first over all of them, so no head's
+      // longest tile starts late (the grid is short and the tail would dominate).
       const int hpx = p.BH / 8;
       const int x = bid % 8, sl = bid / 8;
-      bh = x * hpx + sl / p.ntiles;
-      tile = p.ntiles - 1 - sl % p.ntiles;
+      if (p.interleave) {
+        bh = x * hpx + sl % hpx;
+        tile = p.ntiles - 1 - sl / hpx;
+      } else {
+        bh = x * hpx + sl / p.ntiles;
+        tile = p.ntiles - 1 - sl % p.ntiles;
+      }
     } else {
       bh = bid % p.BH;
       tile = p.ntiles - 1 - bid / p.BH;
@@ -743,11 +755,21 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
   }
 }
 
+// Tile order of an XCD (see the kernel): the heads' tiles in turn below this many query
+// tiles per head, one head at a time above.  Measured on one MI355X (fused attention):
+// L = 8192 keep 0.5 (11 tiles) 0.212 -> 0.177 ms, the planted L = 65536 keep 0.1 layer (18)
+// 0.875 -> 0.832, L = 32768 keep 0.25 (22) 0.660 -> 0.638, L = 131072 keep 0.1 (35) 1.479 ->
+// 1.425; at keep 0.25 (86 tiles) interleaving lost 1% (compact kernel 6%): long rows need the
+// one-head-per-XCD L2 reuse.
+constexpr int kInterleaveBelowTiles = 48;
+int attn_interleave(int ntiles) { return ntiles < kInterleaveBelowTiles ? 1 : 0; }
+
 template <int D, int NW, int MODE, int HPW = 1>
 hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW / HPW * BF16_WQ;
   p.BH = B * H / HPW;                             // head groups (the adaptive paths run HPW = 1)
   p.ntiles = (p.n + BM - 1) / BM;
+  p.interleave = attn_interleave(p.ntiles);
   int64_t blocks = (int64_t)p.BH * p.ntiles;
   if (MODE == ATT_FUSED && p.counts && p.plan) {
     p.plan_cap = (p.BH + 7) / 8;
