@@ -662,16 +662,16 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
       auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          float a0 = 0.f, a1 = 0.f;
+          float pr[8];
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][qb][i], c, -m[qb]));
-              if (i & 1) a1 += pr; else a0 += pr;
-              pf[qb][4 * kk + i] = static_cast<__bf16>(pr);
+              pr[4 * kk + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][qb][i], c, -m[qb]));
+              pf[qb][4 * kk + i] = static_cast<__bf16>(pr[4 * kk + i]);
             }
-          ls[qb] = a0 + a1;
+          // The lane's 8 probabilities summed as a tree (7 additions, no chain through zero).
+          ls[qb] = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
         }
       };
       probs();
