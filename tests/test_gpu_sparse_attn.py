@@ -93,3 +93,31 @@ def test_copy_of_unkept_rows_all_keep_ratios():
             sel = sel.repeat_interleave(8 // idx.shape[1], dim=1).permute(0, 2, 1)
             assert not torch.isnan(out.float()).any(), (keep, per_kv)
             assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16)), (keep, per_kv)
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,keep,W,ns,per_kv", [
+    (1, 32, 8, 4096, 128, 400, 64, 4, False),   # copy inside the attention launch (64 rows per step)
+    (3, 4, 2, 70, 128, 20, 8, 2, False),        # steps crossing batch entries (16 positions per step)
+    (2, 8, 2, 3000, 64, 900, 64, 4, True),      # d = 64: 128 rows per step, per KV head
+    (1, 6, 2, 2000, 128, 700, 64, 4, False),    # 6 heads do not divide a step: separate copy kernel
+    (2, 2, 1, 20, 128, 10, 4, 1, False),        # L below a step's positions: separate copy kernel
+    (1, 16, 4, 1500, 128, 1500, 64, 4, False),  # every row kept: nothing to copy
+])
+def test_out_of_place_equals_in_place(B, H, Hkv, L, d, keep, W, ns, per_kv):
+    # The out-of-place forward copies the rows no head keeps (inside the attention launch
+    # where the shape allows, else as its own kernel) and the attention writes the kept
+    # rows; the in-place forward leaves unkept rows untouched.  Both must give the same
+    # bytes, and every unkept row must equal the residual.
+    x = workloads.small_random(B, H, Hkv, L, d, seed=B * L + H, dtype="bf16")
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    out = torch.full_like(r, float("nan"))
+    _, _, idx = tsa.forward(q, k, v, r, keep, W, ns, out=out, return_scores=True, per_kv_head=per_kv)
+    r_in = r.clone()
+    tsa.forward(q, k, v, r_in, keep, W, ns, out=r_in, per_kv_head=per_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r_in.view(torch.int16))
+    sel = torch.zeros(B, idx.shape[1], L, dtype=torch.bool, device="cuda")
+    sel.scatter_(2, idx.long(), True)
+    sel = sel.repeat_interleave(H // idx.shape[1], dim=1).permute(0, 2, 1)
+    assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16))
+    print(f"B {B} H {H} L {L} d {d} keep {keep}: {int((~sel).sum())} unkept rows copied", flush=True)

@@ -223,9 +223,15 @@ tsa_status forward_run(const tsa_desc& d, const void* q, const void* k, const vo
   if (fused_forward(d)) {
     // Rows a head does not keep are the residual (copied out of place, untouched in place);
     // the attention epilogue writes residual + O into the kept rows.
-    if (!in_place) TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
-    if (d.keep == 0) return TSA_OK;
-    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, f.plan), residual, out, s), s);
+    // Out of place the attention launch also copies the unkept rows (on its first
+    // workgroups, overlapping the attention).
+    if (d.keep == 0) {
+      if (!in_place) return after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s);
+      return TSA_OK;
+    }
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, f.plan), residual, out,
+                                               in_place ? nullptr : inv, s),
+                        s);
   }
   if (d.keep > 0) {
     TSA_TRY(after_launch(tsa::launch_gather_qkv(d, q, k, v, idx, qh, kh, vh, s), s));
@@ -466,12 +472,13 @@ tsa_status tsa_sparse_attn(const tsa_desc* desc, const void* q, const void* k, c
   }
   int32_t* inv = at<int32_t>(ws, y.inv);
   if (fused_forward(d)) {
-    if (!in_place) {
-      TSA_TRY(after_launch(tsa::launch_build_inverse(d, idx, inv, s), s));
-      TSA_TRY(after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s));
+    if (!in_place) TSA_TRY(after_launch(tsa::launch_build_inverse(d, idx, inv, s), s));
+    if (d.keep == 0) {
+      if (!in_place) return after_launch(tsa::launch_copy_unselected(d, inv, residual, out, s), s);
+      return TSA_OK;
     }
-    if (d.keep == 0) return TSA_OK;
-    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, y.plan), residual, out, s),
+    return after_launch(tsa::launch_attn_fused(d, q, k, v, idx, counts, at<int32_t>(ws, y.plan), residual, out,
+                                               in_place ? nullptr : inv, s),
                         s);
   }
   void* qh = at<char>(ws, y.qh);

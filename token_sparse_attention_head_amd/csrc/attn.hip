@@ -42,6 +42,11 @@
 //   With adaptive budgets (rows differ per head) attn_plan_kernel first deals the heads,
 //   sorted by attention work, to the XCDs in snake order, keeping that locality while
 //   the XCDs get equal work.
+// * Out of place, the fused launch also copies the residual rows no head keeps: its first
+//   workgroups (64, eight per XCD) stream those rows with buffer accesses, two steps in
+//   flight per wave, while the other CUs run the attention, so the copy's memory latency
+//   hides behind the attention's arithmetic (a separate copy kernel would occupy every CU
+//   for its whole run).
 #include <cstdlib>
 
 #include "common.h"
@@ -72,6 +77,9 @@ struct AttnParams {
   int plan_cap;            // heads per XCD list in the plan
   int L;                   // fused forward: sequence length (index-list entries are clamped below it)
   int interleave;          // 1: an XCD deals the tiles of its heads in turn (longest first over all of them)
+  const int32_t* inv;      // fused forward out of place: [B][H / idx_div][L] kept-row map, < 0 at rows to copy
+  int copy_wgs;            // with inv: the first copy_wgs workgroups copy those rows of res to o
+  int B;                   // batch entries
 };
 
 // Plan of the fused attention under adaptive budgets (rows differ per head).  A head's
@@ -430,6 +438,137 @@ __device__ __forceinline__ f32x4 mfma16(f32x4 c, bf16x8 a, bf16x8 b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Copy of the residual rows no subset keeps, run by the first workgroups of the fused
+// attention launch so that it overlaps the attention on the other CUs: the copy is bound by
+// memory latency and needs few CUs, the attention by the matrix and vector units.  Rows are
+// (position, head) rows of d elements in memory order.  Every wave of a copy workgroup
+// streams a contiguous run of rows on its own (no barriers: a workgroup barrier waits for
+// every load in flight).  A step is CP_UNROLL wave-wide 16-byte accesses, each covering
+// 64 / (row vectors) rows; the rows whose kept-row map entry is negative are read and
+// written.  Two steps of data are in flight: the next step's reads are issued before this
+// step's writes, and the map entries (one load per lane for a step's rows, handed to the
+// lanes that copy each row by cross-lane reads) two steps ahead.
+#ifndef TSA_COPY_WGS
+#define TSA_COPY_WGS 64
+#endif
+#ifndef TSA_COPY_UNROLL
+#define TSA_COPY_UNROLL 16
+#endif
+constexpr int kCopyWgs = TSA_COPY_WGS;     // copy workgroups (a multiple of 8: one share per XCD)
+constexpr int CP_UNROLL = TSA_COPY_UNROLL;
+
+template <int ROWB>
+constexpr int copy_rows_per_step() { return TSA_WAVE / (ROWB / 16) * CP_UNROLL; }
+
+// A step covers whole positions (the host launches the in-attention copy only when the
+// heads H divide the step's rows, L >= the step's positions and the rows fit 32 bits), so a
+// lane's head and position offset within a step are fixed; the position (b, pos) of the
+// next step to fetch advances by the step's positions.
+template <int ROWB, int NT>
+__device__ __forceinline__ void copy_unkept_rows(const AttnParams& p, int wg) {
+  constexpr int VPR = ROWB / 16;                   // 16-byte vectors per row
+  constexpr int RPI = TSA_WAVE / VPR;              // rows per wave-wide access
+  constexpr int U = CP_UNROLL;
+  constexpr int RPS = copy_rows_per_step<ROWB>();  // rows per step
+  constexpr int EPL = RPS / TSA_WAVE;              // map entries per lane per step
+  static_assert(RPS % TSA_WAVE == 0 && TSA_WAVE % RPI == 0, "step shape");
+  const int lane = lane_id();
+  // Wave-uniform (the buffer views below must live in scalar registers).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / TSA_WAVE);
+  const int sub = lane / VPR, vec = lane % VPR;
+  const int H = p.H, L = p.L, R = p.H / p.idx_div;
+  const int PPS = RPS / H;                         // positions per step
+  const uint32_t npos = (uint32_t)p.B * (uint32_t)L;
+  const uint32_t nw = (uint32_t)p.copy_wgs * (NT / TSA_WAVE);
+  const uint32_t seg = ((npos + nw - 1) / nw + PPS - 1) / PPS * PPS;   // positions per wave
+  const uint32_t g0 = ((uint32_t)wg * (NT / TSA_WAVE) + wave) * seg;
+  if (g0 >= npos) return;
+  const uint32_t g1 = g0 + seg < npos ? g0 + seg : npos;
+  const uint32_t row_end = g1 * (uint32_t)H;
+  int po[EPL], hs[EPL];                            // position offset and subset of the lane's map entries
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int t = i * TSA_WAVE + lane;
+    po[i] = t / H;
+    hs[i] = (t % H) / p.idx_div;
+  }
+  // Buffer views of the wave's run of rows: a lane whose row is kept (or past the run)
+  // gets an offset beyond the range, so its read returns 0 and its write is dropped, with
+  // no branch (branches around the accesses would make the compiler wait for every access
+  // in flight where they join).
+  const uint32_t row0 = g0 * (uint32_t)H;
+  const uint32_t run_bytes = (row_end - row0) * (uint32_t)ROWB;
+  constexpr uint32_t OUTSIDE = 0x80000000u;
+  constexpr int BUF_FLAGS = 0x00020000;            // buffer resource word 3: 32-bit data format, raw access
+  constexpr int NT_POLICY = 2;                     // non-temporal
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(p.res)) + (int64_t)row0 * ROWB, 0, (int)run_bytes, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<char*>(p.o) + (int64_t)row0 * ROWB, 0, (int)run_bytes, BUF_FLAGS);
+  int b = (int)(g0 / (uint32_t)L), pos = (int)(g0 % (uint32_t)L);
+  // Map entries of the step at (b, pos) whose first row is r0 (0, i.e. kept, past the run);
+  // then (b, pos) moves to the next step.  The read index is always in range.
+  auto fetch = [&](int (&ent)[EPL], uint32_t r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      int pj = pos + po[i], bj = b;
+      if (pj >= L) { pj -= L; ++bj; }
+      bj = bj < p.B ? bj : p.B - 1;
+      const int e = p.inv[((int64_t)bj * R + hs[i]) * L + pj];
+      ent[i] = r0 + i * TSA_WAVE + lane < row_end ? e : 0;
+    }
+    pos += PPS;
+    if (pos >= L) { pos -= L; ++b; }
+  };
+  // Access j of a step copies row j * RPI + sub of the step: its byte offset in the run,
+  // or OUTSIDE.
+  auto offsets = [&](uint32_t (&o)[U], const int (&ent)[EPL], uint32_t r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int e = __shfl(ent[j * RPI / TSA_WAVE], (j * RPI) % TSA_WAVE + sub, TSA_WAVE);
+      o[j] = e < 0 ? (r0 - row0 + j * RPI + sub) * (uint32_t)ROWB + vec * 16 : OUTSIDE;
+    }
+  };
+  auto load = [&](u32x4 (&v)[U], const uint32_t (&o)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, o[j], 0, NT_POLICY);
+  };
+  auto store = [&](const u32x4 (&v)[U], const uint32_t (&o)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) __builtin_amdgcn_raw_buffer_store_b128(v[j], dst, o[j], 0, NT_POLICY);
+  };
+  uint32_t r = row0;
+  int entA[EPL], entB[EPL];
+  uint32_t oA[U], oB[U];
+  u32x4 vA[U], vB[U];
+  fetch(entA, r);                                  // entries of steps 0 and 1
+  fetch(entB, r + RPS);
+  offsets(oA, entA, r);
+  load(vA, oA);                                    // step 0 in flight
+  fetch(entA, r + 2 * RPS);                        // entries of step 2
+  // Steps past the run have no negative entries, so the pairs need no tail.
+  for (; r < row_end; r += 2 * RPS) {
+    offsets(oB, entB, r + RPS);
+    load(vB, oB);                                  // step k + 1 in flight
+    store(vA, oA);                                 // step k written
+    fetch(entB, r + 3 * RPS);
+    offsets(oA, entA, r + 2 * RPS);
+    load(vA, oA);                                  // step k + 2 in flight
+    store(vB, oB);                                 // step k + 1 written
+    fetch(entA, r + 4 * RPS);
+  }
+}
+
+// Whether the fused launch can carry the copy (else the forward launches it on its own).
+template <int ROWB>
+bool copy_fits(int B, int L, int H) {
+  constexpr int RPS = copy_rows_per_step<ROWB>();
+  // Rows fit 32 bits, and a copy wave's run (at least 512 waves) stays below 2^31 bytes.
+  const int64_t rows = (int64_t)B * L * H;
+  return H > 0 && RPS % H == 0 && L >= RPS / H && rows < ((int64_t)1 << 32) - RPS &&
+         rows / (8 * (kCopyWgs < 64 ? kCopyWgs : 64)) * ROWB < ((int64_t)1 << 30);
+}
+
 constexpr int BF16_QB = 3;                 // 16-row query blocks per wave
 constexpr int BF16_WQ = 16 * BF16_QB;      // query rows per wave
 
@@ -474,7 +613,14 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
 
   int bh, tile, n = p.n;
   {
-    const int bid = blockIdx.x;
+    int bid = blockIdx.x;
+    if (FUSED && p.copy_wgs > 0) {
+      if (bid < p.copy_wgs) {
+        copy_unkept_rows<2 * D, NT>(p, bid);
+        return;
+      }
+      bid -= p.copy_wgs;
+    }
     if (FUSED && p.counts && p.plan) {
       // Rows differ per subset: the XCD's head list from attn_plan_kernel, one head after
       // another, longest tiles first.
@@ -767,6 +913,7 @@ int attn_interleave(int ntiles) { return ntiles < kInterleaveBelowTiles ? 1 : 0;
 template <int D, int NW, int MODE, int HPW = 1>
 hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
   constexpr int BM = NW / HPW * BF16_WQ;
+  p.B = B;
   p.BH = B * H / HPW;                             // head groups (the adaptive paths run HPW = 1)
   p.ntiles = (p.n + BM - 1) / BM;
   p.interleave = attn_interleave(p.ntiles);
@@ -776,6 +923,15 @@ hipError_t launch_attn_bf16(AttnParams p, int B, int H, hipStream_t s) {
     attn_plan_kernel<<<1, PLAN_THREADS, 0, s>>>(p.counts, const_cast<int32_t*>(p.plan), p.BH, p.H, p.idx_div, BM,
                                                 p.plan_cap);
     blocks = 8ll * p.plan_cap * p.ntiles;
+  }
+  p.copy_wgs = 0;
+  if (MODE == ATT_FUSED && p.inv) {
+    if (!copy_fits<2 * D>(B, p.L, H)) return hipErrorInvalidValue;
+    // Copy workgroups first (dispatched first, one per CU), a multiple of 8 so that the
+    // attention workgroups keep their XCD (workgroup IDs are dealt to the XCDs in turn).
+    const int64_t rows = (int64_t)B * p.L * H;    // at least 4096 rows per copy workgroup
+    p.copy_wgs = (int)std::min<int64_t>(kCopyWgs, (rows + 8 * 4096 - 1) / (8 * 4096) * 8);
+    blocks += p.copy_wgs;
   }
   attn_bf16_kernel<D, NW, MODE, HPW><<<(unsigned)blocks, NW * TSA_WAVE, 0, s>>>(p);
   return hipGetLastError();
@@ -832,10 +988,17 @@ size_t attn_plan_bytes(const tsa_desc& d) {
 }
 
 hipError_t launch_attn_fused(const tsa_desc& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             const int32_t* counts, int32_t* plan, const void* res, void* out, hipStream_t s) {
+                             const int32_t* counts, int32_t* plan, const void* res, void* out, const int32_t* inv,
+                             hipStream_t s) {
   if (d.dtype != TSA_BF16) return hipErrorInvalidValue;
+  if (inv && !(d.d == 128 ? copy_fits<256>(d.B, d.L, d.H) : copy_fits<128>(d.B, d.L, d.H))) {
+    // Shapes the in-launch copy does not cover: the copy runs as its own kernel first.
+    const hipError_t e = launch_copy_unselected(d, inv, res, out, s);
+    if (e != hipSuccess) return e;
+    inv = nullptr;
+  }
   AttnParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res; p.counts = counts;
+  p.q = q; p.k = k; p.v = v; p.o = out; p.idx = idx; p.res = res; p.counts = counts; p.inv = inv;
   p.plan = attn_plan_bytes(d) ? plan : nullptr;
   p.idx_div = heads_per_subset(d);
   p.n = d.keep;
