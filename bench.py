@@ -17,6 +17,7 @@ JSON file given by --detail.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -78,6 +79,16 @@ class Timer:
         b.record(s)
         t.cuda.synchronize()
         return a.elapsed_time(b) / reps
+
+    def span(self, fn, min_reps, span_ms, max_reps=1000):
+        """Mean ms of back-to-back calls over about `span_ms` of GPU time (at least min_reps
+        calls), after about a third of that span of untimed calls: short calls are then timed
+        in steady state, not in the clock ramp after an idle GPU.  Returns (ms, calls)."""
+        est = max(self.run(fn, 1), 1e-3)
+        for _ in range(min(max_reps, math.ceil(span_ms / 3 / est))):
+            fn()
+        n = int(min(max_reps, max(min_reps, math.ceil(span_ms / est))))
+        return self.run(fn, n), n
 
     def each(self, fn, reps, flush=None):
         """ms of every call timed alone (events around each call); `flush` runs untimed
@@ -171,9 +182,16 @@ def graph_step_ms(torch, timer, step, steps):
     return ms
 
 
-def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_head=False, full=True):
+STEP_SPAN_MS = 300.0    # GPU time each sweep or config step measurement covers
+STAGE_SPAN_MS = 40.0    # and each stage measurement
+
+
+def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_head=False, full=True, span=False):
     """One workload: the step (tsa_forward) and, with `full`, every stage through its own
-    entry point, the fused attention alone, drift, cold runs and the dense reference."""
+    entry point, the fused attention alone, drift, cold runs and the dense reference.
+    span=False: exactly `warmup` untimed and `steps` timed steps (the headline); span=True:
+    steps over STEP_SPAN_MS of GPU time after a third of that untimed (the sweep and the
+    other workloads, whose steps are short)."""
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, r = (torch.from_numpy(x[n]).to(dt).cuda() for n in "qkvr")
     desc = tsa.desc_for(q, k, w.keep, w.W, w.n_sink, per_kv_head=per_kv_head)
@@ -188,11 +206,16 @@ def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_he
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms_events = timer.run(step, steps)
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    if span:
+        t0 = time.perf_counter()
+        ms_events, steps = timer.span(step, steps, STEP_SPAN_MS)
+        wall_ms = None
+    else:
+        t0 = time.perf_counter()
+        ms_events = timer.run(step, steps)
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = {"workload": w.name, "subsets": "per_kv_head" if per_kv_head else "per_head", "keep": w.keep,
-           "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events, "wall_ms_per_step": wall_ms,
+           "ratio": round(w.keep / w.L, 4), "ms_per_step": ms_events, "steps": steps, "wall_ms_per_step": wall_ms,
            "tokens_per_s": B * L / (ms_events / 1e3)}
     res["step_stats_ms"] = stats(timer.each(step, steps))      # the same steps timed one by one
     res["graph_ms_per_step"] = graph_ms = graph_step_ms(torch, timer, step, steps)
@@ -227,7 +250,7 @@ def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_he
     stage_ms = {}
     for name, fn in stages.items():
         fn()
-        stage_ms[name] = timer.run(fn, reps)
+        stage_ms[name] = timer.span(fn, reps, STAGE_SPAN_MS)[0]
     res["stage_ms"] = stage_ms
     a = algorithmic(w, per_kv_head)
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -297,7 +320,6 @@ def adaptive_case(tsa, torch, timer, w, steps, reps, dense_ms):
     (sum over heads of 2*d*K_h*(K_h+1)), and a fixed-budget step with the same total
     attention work spread evenly (keep = sqrt(mean K_h*(K_h+1))), which shows what the
     uneven rows cost."""
-    import math
     import workloads
     x = workloads.make_inputs(w)
     q, k, v, r = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in "qkvr")
@@ -530,7 +552,8 @@ def main():
                 if name == w.name and not per_kv:
                     continue
                 wi = workloads.WORKLOADS[name]
-                res = gpu_case(tsa, torch, timer, wi, x, args.stage_reps, sub_steps, 1, False, per_kv, full=False)
+                res = gpu_case(tsa, torch, timer, wi, x, args.stage_reps, sub_steps, 1, False, per_kv, full=False,
+                               span=True)
                 sweep.append(with_dense_ratios(res, dense_ms))
                 log(brief(res))
         wa = workloads.WORKLOADS["bf16_L128k_tau0.2_graded"]
@@ -545,7 +568,7 @@ def main():
             wi = workloads.WORKLOADS[name]
             xi = workloads.make_inputs(wi)
             res = gpu_case(tsa, torch, timer, wi, xi, args.stage_reps, max(5, args.steps // 2), 1,
-                           name == "bf16_L32k_r0.25" and not args.no_dense)
+                           name == "bf16_L32k_r0.25" and not args.no_dense, span=True)
             del xi
             res = with_dense_ratios(res, res.get("dense_ms"))
             res["shape"] = {"B": wi.B, "L": wi.L, "H": wi.H, "Hkv": wi.Hkv, "d": wi.d, "W": wi.W,
