@@ -296,6 +296,114 @@ __global__ __launch_bounds__(SEL_WG) void sel_write_kernel(const float* __restri
 }
 
 
+__device__ unsigned long long block_inclusive_scan64(unsigned long long x, unsigned long long* wave_tot);
+
+// ---- one-workgroup select for rows of at most 16384 positions ------------------------
+//
+// The same rule and the same three radix passes, in one launch: a 1024-thread workgroup per
+// row holds the row's scores in registers (thread t owns the PER consecutive positions
+// [t*PER, (t+1)*PER)), builds each pass's histogram in LDS and scans it itself, then counts
+// its strict and equal positions; one block-wide scan of the (strict, equal) counts gives
+// every thread the offset of its positions, which it writes in ascending order, ties at T
+// to the lowest positions.  For short rows the nine launches of the multi-workgroup path
+// cost more than the work: 32 rows, L = 8192: 34 us, here 14 us; at L = 32768 one workgroup
+// per row is slower (45 us against 31: few workgroups, and the LDS histogram atomics of a
+// row contend on its few occupied bins).
+constexpr int SEL_ROW_MAX_L = 16384;
+
+template <int PER>
+__global__ __launch_bounds__(SEL_THREADS) void sel_row_kernel(const float* __restrict__ scores,
+                                                              int32_t* __restrict__ idx, int32_t* __restrict__ inv,
+                                                              const int32_t* __restrict__ budgets, SelGeom g) {
+  __shared__ uint32_t hist[SEL_MAX_BINS];
+  __shared__ uint32_t wave_tot[SEL_WAVES];
+  __shared__ unsigned long long wave_tot64[SEL_WAVES];
+  __shared__ uint32_t found[2];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + (int64_t)row * g.L);
+  const int j0 = tid * PER;
+  uint32_t u[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) u[p] = j0 + p < g.L ? key[j0 + p] : 0u;
+  const int keep = row_keep(budgets, row, g);
+  const int n_cand = g.c1 - g.c0;
+  uint32_t need = (uint32_t)(keep - (g.L - n_cand));
+  const bool take_all = (int)need >= n_cand, take_none = need == 0;
+  uint32_t prefix = 0, pmask = 0;
+  if (!take_all && !take_none) {
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = sel_shift(pass), nb = sel_bins(pass);
+      for (int i = tid; i < nb; i += SEL_THREADS) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int j = j0 + p;
+        if (j >= g.c0 && j < g.c1 && (u[p] & pmask) == prefix) atomicAdd(&hist[(u[p] >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      // Bins in descending order; thread t owns ranks [t*per, (t+1)*per).
+      const int per = nb / SEL_THREADS;
+      uint32_t cnt[SEL_MAX_BINS / SEL_THREADS];
+      uint32_t local = 0;
+      for (int q = 0; q < per; ++q) {
+        cnt[q] = hist[nb - 1 - (tid * per + q)];
+        local += cnt[q];
+      }
+      const uint32_t incl = block_inclusive_scan(local, wave_tot);
+      const uint32_t excl = incl - local;
+      if (excl < need && need <= incl) {
+        uint32_t cum = excl;
+        for (int q = 0; q < per; ++q) {
+          if (cum + cnt[q] >= need) {
+            found[0] = need - cum;
+            found[1] = (uint32_t)(nb - 1 - (tid * per + q));
+            break;
+          }
+          cum += cnt[q];
+        }
+      }
+      __syncthreads();
+      need = found[0];
+      prefix |= found[1] << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      __syncthreads();                             // found and hist are rewritten next pass
+    }
+  }
+  SelRule rule;
+  rule.c0 = g.c0;
+  rule.c1 = g.c1;
+  rule.T = prefix;
+  rule.take_all = take_all;
+  rule.take_none = take_none;
+  const uint32_t need_eq = (take_all || take_none) ? 0u : need;
+  uint32_t n_st = 0, n_eq = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    bool st, eq;
+    rule.classify(j0 + p, j0 + p < g.L, u[p], st, eq);
+    n_st += st;
+    n_eq += eq;
+  }
+  const unsigned long long mine = ((unsigned long long)n_st << 32) | n_eq;
+  const unsigned long long before = block_inclusive_scan64(mine, wave_tot64) - mine;
+  uint32_t pos = (uint32_t)(before >> 32) + min(need_eq, (uint32_t)before);
+  uint32_t eq_rank = (uint32_t)before;
+  int32_t* row_idx = idx + (int64_t)row * g.keep;
+  int32_t* row_inv = inv ? inv + (int64_t)row * g.L : nullptr;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int j = j0 + p;
+    bool st, eq;
+    rule.classify(j, j < g.L, u[p], st, eq);
+    const bool take = st || (eq && eq_rank < need_eq);
+    eq_rank += eq;
+    if (take && pos < (uint32_t)keep) row_idx[pos] = j;
+    if (row_inv && j < g.L) row_inv[j] = (take && pos < (uint32_t)keep) ? (int32_t)pos : -1;
+    pos += take;
+  }
+  for (int t = keep + tid; t < g.keep; t += SEL_THREADS) row_idx[t] = -1;   // adaptive budget below keep
+}
+
 // ---- adaptive budgets (token coverage tau) ------------------------------------------
 //
 // The paper page "Token Sparse Attention: Efficient Long-Context Inference with
@@ -581,6 +689,16 @@ hipError_t launch_select(const tsa_desc& d, const float* scores, int32_t* idx, i
     int32_t* out = budgets ? budgets : reinterpret_cast<int32_t*>(base + y.budgets);
     budget_rows(d, src, out, y, base, s);
     counts_in = out;
+  }
+  if (d.L <= SEL_ROW_MAX_L) {
+    // Short rows: the whole select in one launch, one workgroup per row.
+    const int per = (d.L + SEL_THREADS - 1) / SEL_THREADS;
+    if (per <= 1) sel_row_kernel<1><<<rows, SEL_THREADS, 0, s>>>(src, idx, inv, counts_in, g);
+    else if (per <= 2) sel_row_kernel<2><<<rows, SEL_THREADS, 0, s>>>(src, idx, inv, counts_in, g);
+    else if (per <= 4) sel_row_kernel<4><<<rows, SEL_THREADS, 0, s>>>(src, idx, inv, counts_in, g);
+    else if (per <= 8) sel_row_kernel<8><<<rows, SEL_THREADS, 0, s>>>(src, idx, inv, counts_in, g);
+    else sel_row_kernel<16><<<rows, SEL_THREADS, 0, s>>>(src, idx, inv, counts_in, g);
+    return hipGetLastError();
   }
   uint32_t* state = reinterpret_cast<uint32_t*>(base + y.state);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + y.hist);
