@@ -563,9 +563,10 @@ __device__ __forceinline__ void copy_unkept_rows(const AttnParams& p, int wg) {
 template <int ROWB>
 bool copy_fits(int B, int L, int H) {
   constexpr int RPS = copy_rows_per_step<ROWB>();
-  // Rows fit 32 bits, and a copy wave's run (at least 512 waves) stays below 2^31 bytes.
+  // Rows, and the rows of the steps fetched up to four past a run's end, fit 32 bits; a copy
+  // wave's run (at least 512 waves) stays below 2^31 bytes.
   const int64_t rows = (int64_t)B * L * H;
-  return H > 0 && RPS % H == 0 && L >= RPS / H && rows < ((int64_t)1 << 32) - RPS &&
+  return H > 0 && RPS % H == 0 && L >= RPS / H && rows < ((int64_t)1 << 32) - 8 * RPS &&
          rows / (8 * (kCopyWgs < 64 ? kCopyWgs : 64)) * ROWB < ((int64_t)1 << 30);
 }
 
