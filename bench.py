@@ -256,6 +256,9 @@ def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_he
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     rate = {
         "score": ("mfma", a["score_flops"] / (stage_ms["score"] * 1e-3) / 1e12, peak_mm),
+        # the score sits near the ridge: its bytes (K once, the window queries, the scores
+        # written) against the HBM roof as well
+        "score_hbm": ("hbm", a["score_bytes"] / (stage_ms["score"] * 1e-3) / 1e9, PEAK_HBM_GBS),
         "select": ("hbm", a["select_bytes"] / (stage_ms["select"] * 1e-3) / 1e9, PEAK_HBM_GBS),
         "fused_attn": ("mfma", a["attn_flops"] / (stage_ms["fused_attn"] * 1e-3) / 1e12, peak_mm),
     }
@@ -300,6 +303,7 @@ def gpu_case(tsa, torch, timer, w, x, reps, steps, warmup, with_dense, per_kv_he
         dms = timer.run(dense, max(2, reps // 2))
         res["dense_ms"] = dms
         res["dense_tflops"] = a["dense_flops"] / (dms * 1e-3) / 1e12
+        res["attn_stage_speedup_vs_dense"] = dms / stage_ms["fused_attn"]   # the attention stage alone
         del o
     del ws, comp, out, r2
     return res
@@ -491,7 +495,18 @@ def cpu_baseline(w, x, budget_s=20.0):
                       f"rows per head scaled by causal row cost; {wall:.0f} s on {workers} single-threaded workers",
             "detail": {"seconds_per_step_extrapolated": step_s, "cpu_seconds_extrapolated": cpu_s,
                        "cpu_seconds_per_stage": per_stage, "measured_wall_s": wall,
-                       "host": {"cpu_model": cpu_model, "affinity_cores": cores, "numpy": np.__version__}}}
+                       "host": {"cpu_model": cpu_model, "affinity_cores": cores, "numpy": np.__version__,
+                                "blas": _blas_info()}}}
+
+
+def _blas_info():
+    """BLAS libraries numpy loaded (name, version, threads), as threadpoolctl reports them."""
+    try:
+        from threadpoolctl import threadpool_info
+        return [{k: i.get(k) for k in ("internal_api", "version", "num_threads")} for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        return "unknown"
 
 
 # ---- main -------------------------------------------------------------------------------
