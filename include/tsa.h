@@ -222,8 +222,9 @@ tsa_status tsa_forward_noalloc(const tsa_desc* desc, const void* q, const void* 
  * tsa_select writes it: ascending positions in [0, L), then (tau > 0 only) -1 padding;
  * the row counts K_r are read off the padding.  bf16 runs one attention kernel that
  * reads the rows through idx and writes residual + O into the kept rows (no compact
- * tensors); an out-of-place output first gets the residual at the positions no head
- * keeps.  fp32 runs the three stages through compact tensors in the workspace.  out ==
+ * tensors); out of place, the same launch copies the residual to the rows no head keeps
+ * (on workgroups of its own, while the others run the attention).  fp32 runs the three
+ * stages through compact tensors in the workspace.  out ==
  * residual (the same pointer) updates in place; any other overlap of out with an input
  * is TSA_ERR_ALIAS.  Positions outside [0, L) in a kept row give unspecified results but
  * no access outside the tensors.  Workspace: TSA_OP_SPARSE_ATTN. */
