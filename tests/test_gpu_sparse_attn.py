@@ -121,3 +121,38 @@ def test_out_of_place_equals_in_place(B, H, Hkv, L, d, keep, W, ns, per_kv):
     sel = sel.repeat_interleave(H // idx.shape[1], dim=1).permute(0, 2, 1)
     assert torch.equal(out[~sel].view(torch.int16), r[~sel].view(torch.int16))
     print(f"B {B} H {H} L {L} d {d} keep {keep}: {int((~sel).sum())} unkept rows copied", flush=True)
+
+
+def _random_shapes(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        H = Hkv * G
+        if H > 64:
+            continue
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 4))
+        L = int(rng.integers(70, 3000))
+        W = int(rng.choice([1, 16, 64]))
+        ns = int(rng.integers(0, 5))
+        forced = min(ns, L) + min(W, L)
+        keep = int(rng.integers(min(forced, L), L + 1))
+        per_kv = bool(rng.integers(0, 2)) and G > 1
+        out.append((B, H, Hkv, L, d, keep, W, ns, per_kv))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,keep,W,ns,per_kv", _random_shapes(14))
+def test_out_of_place_equals_in_place_random_shapes(B, H, Hkv, L, d, keep, W, ns, per_kv):
+    # Seeded random shapes over both copy paths (heads dividing a step's rows or not, rows
+    # crossing batch entries, every keep ratio): out of place equals in place bit for bit.
+    x = workloads.small_random(B, H, Hkv, L, d, seed=B * L + H + d, dtype="bf16")
+    q, k, v, r = (dev(x[n], "bf16") for n in "qkvr")
+    out = torch.full_like(r, float("nan"))
+    tsa.forward(q, k, v, r, keep, W, ns, out=out, per_kv_head=per_kv)
+    r_in = r.clone()
+    tsa.forward(q, k, v, r_in, keep, W, ns, out=r_in, per_kv_head=per_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r_in.view(torch.int16))
