@@ -307,8 +307,9 @@ __device__ unsigned long long block_inclusive_scan64(unsigned long long x, unsig
 // every thread the offset of its positions, which it writes in ascending order, ties at T
 // to the lowest positions.  For short rows the nine launches of the multi-workgroup path
 // cost more than the work: 32 rows, L = 8192: 34 us, here 14 us; at L = 32768 one workgroup
-// per row is slower (45 us against 31: few workgroups, and the LDS histogram atomics of a
-// row contend on its few occupied bins).
+// per row is slower (45 us against 31: 32 workgroups on 256 CUs each do a whole row's passes
+// serially; four histogram copies per workgroup, a quarter of the threads each, made no
+// difference, so it is not the atomics).
 constexpr int SEL_ROW_MAX_L = 16384;
 
 template <int PER>
