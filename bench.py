@@ -147,7 +147,6 @@ def algorithmic(w, per_kv_head=False):
     e = 2 if w.dtype == "bf16" else 4
     B, H, Hkv, L, d, K, W = w.B, w.H, w.Hkv, w.L, w.d, w.keep, min(w.W, w.L)
     R = Hkv if per_kv_head else H
-    unkept_rows = B * H * (L - K)          # every query head keeps K rows, per head or per KV head
     return {
         "score_flops": 2.0 * B * H * d * sum(L - W + r + 1 for r in range(W)),
         "score_bytes": B * Hkv * L * d * e + B * H * W * d * e + 4 * B * H * L,
@@ -156,9 +155,6 @@ def algorithmic(w, per_kv_head=False):
         "gather_bytes": 2 * (B * H + 2 * B * R) * K * d * e + 4 * B * H * K,
         "attn_flops": 2.0 * B * H * d * K * (K + 1),
         "scatter_bytes": 2 * B * L * H * d * e + B * H * K * d * e + 4 * B * H * L,
-        # fused forward, out of place: the residual rows no head keeps read and written, the
-        # inverse map read
-        "copy_bytes": 2 * unkept_rows * d * e + 4 * B * R * L,
         "dense_flops": 2.0 * B * H * d * L * (L + 1),
         "drift_bytes": 2 * B * L * H * d * e,          # both hidden-state tensors read once
     }
