@@ -135,33 +135,53 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(const T* __restrict__ 
   }
 }
 
-// Folds the per-chunk (max, sum) of every window row into (m_i, 1 / l_i).  Four threads
-// per row each fold a strided quarter of the chunks, then the first folds the four
-// partials; the order is fixed, so the result is deterministic.
-constexpr int MERGE_PARTS = 4;
-__global__ __launch_bounds__(64 * MERGE_PARTS) void score_merge_kernel(const float2* __restrict__ part,
-                                                                       float2* __restrict__ stat, int nchunk,
-                                                                       int Wp) {
-  __shared__ float2 partial[MERGE_PARTS][64];
-  const int bh = blockIdx.x;
-  const int row = threadIdx.x % 64;
-  const int q = threadIdx.x / 64;
+// Folds the per-chunk (max, sum) of every window row into (m_i, 1 / l_i).  A workgroup takes
+// 16 rows of one (b, h): lane r + 16 s of wave w folds the chunks c = 4 w + s (mod 16) of row r
+// (the 16 rows of a chunk are adjacent in memory), then the four lanes of a row in a wave and
+// the four waves are folded, always in the same order, so the result is deterministic.
+constexpr int MERGE_ROWS = 16;
+constexpr int MERGE_SLICES = 16;
+
+__device__ __forceinline__ void fold_ms(float& M, float& S, float mo, float so) {
+  const float mm = fmaxf(M, mo);
+  S = S * __builtin_amdgcn_exp2f(M - mm) + so * __builtin_amdgcn_exp2f(mo - mm);
+  M = mm;
+}
+
+__global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void score_merge_kernel(const float2* __restrict__ part,
+                                                                               float2* __restrict__ stat,
+                                                                               int nchunk, int Wp) {
+  __shared__ float2 wpart[MERGE_SLICES / 4][MERGE_ROWS];
+  const int groups = (Wp + MERGE_ROWS - 1) / MERGE_ROWS;
+  const int bh = blockIdx.x / groups;
+  const int row = (blockIdx.x % groups) * MERGE_ROWS + threadIdx.x % MERGE_ROWS;
+  const int slice = threadIdx.x / MERGE_ROWS;
   const float2* p = part + (int64_t)bh * nchunk * Wp + row;
   float M = NEG_BIG, S = 0.f;
   if (row < Wp) {
-    for (int c = q; c < nchunk; c += MERGE_PARTS) M = fmaxf(M, p[(int64_t)c * Wp].x);
-    for (int c = q; c < nchunk; c += MERGE_PARTS) {
+    int c = slice;
+    for (; c + 3 * MERGE_SLICES < nchunk; c += 4 * MERGE_SLICES) {   // four chunks in flight
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = p[(int64_t)(c + u * MERGE_SLICES) * Wp];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fold_ms(M, S, v[u].x, v[u].y);
+    }
+    for (; c < nchunk; c += MERGE_SLICES) {
       const float2 v = p[(int64_t)c * Wp];
-      S += v.y * __builtin_amdgcn_exp2f(v.x - M);
+      fold_ms(M, S, v.x, v.y);
     }
   }
-  partial[q][row] = make_float2(M, S);
+  // The four slices of a row in this wave: lanes r, r + 16, r + 32, r + 48.
+  fold_ms(M, S, __shfl_xor(M, 16, TSA_WAVE), __shfl_xor(S, 16, TSA_WAVE));
+  fold_ms(M, S, __shfl_xor(M, 32, TSA_WAVE), __shfl_xor(S, 32, TSA_WAVE));
+  const int wave = threadIdx.x / TSA_WAVE, lane = threadIdx.x % TSA_WAVE;
+  if (lane < MERGE_ROWS) wpart[wave][lane] = make_float2(M, S);
   __syncthreads();
-  if (q == 0 && row < Wp) {
-    float Mt = NEG_BIG;
-    for (int i = 0; i < MERGE_PARTS; ++i) Mt = fmaxf(Mt, partial[i][row].x);
-    float St = 0.f;
-    for (int i = 0; i < MERGE_PARTS; ++i) St += partial[i][row].y * __builtin_amdgcn_exp2f(partial[i][row].x - Mt);
+  if (wave == 0 && lane < MERGE_ROWS && row < Wp) {
+    float Mt = wpart[0][lane].x, St = wpart[0][lane].y;
+#pragma unroll
+    for (int w = 1; w < MERGE_SLICES / 4; ++w) fold_ms(Mt, St, wpart[w][lane].x, wpart[w][lane].y);
     stat[(int64_t)bh * Wp + row] = make_float2(Mt, 1.0f / St);
   }
 }
@@ -229,36 +249,52 @@ __global__ __launch_bounds__(256) void score_pass2_kernel(const T* __restrict__ 
 // ---- bf16 kernels with the K tile staged once per workgroup ------------------------------
 
 constexpr int SBN = 64;       // keys per staged tile
+constexpr int SCORE_BUF_FLAGS = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
 constexpr int SPF = 2;        // tiles in flight in registers
 
-// Cooperative staging of 64-key K tiles of one (b, KV head) into padded LDS rows KP_ bytes
-// apart, NSETS tiles in flight in registers.
+// Cooperative staging of the 64-key K tiles of one (b, KV head) chunk into padded LDS rows
+// KP_ bytes apart, NSETS tiles in flight in registers.  The rows come through a buffer view
+// of the chunk: a lane's byte offset within a tile is fixed, a tile adds a wave-uniform
+// offset, and rows past the sequence fall outside the view and read as zero (their keys
+// are masked by the callers).  So a load costs one add, not a 64-bit address computation.
 template <int D, int KP_, int NSETS = SPF>
 struct KStage {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int LPT = SBN * CPR / 256;        // chunks per thread per tile
   static constexpr int KP = KP_;
-  const char* base;          // K row of position 0 for this (b, KV head), bytes
-  int64_t row_bytes;         // bytes between positions
-  int L, lrow[LPT], lch[LPT], soff[LPT];
+  __amdgpu_buffer_rsrc_t rows;
+  uint32_t tile_bytes;       // bytes between consecutive tiles
+  int last_tile;             // the chunk's last tile; prefetches past it re-read it
+  uint32_t loff[LPT];
+  int soff[LPT];
   u32x4 st[NSETS][LPT];
-  __device__ __forceinline__ void init(const __bf16* k, const ScoreGeom& g, int b, int kvh) {
-    base = reinterpret_cast<const char*>(k + ((int64_t)b * g.L * g.Hkv + kvh) * D);
-    row_bytes = (int64_t)g.Hkv * D * 2;
-    L = g.L;
+  // The chunk's rows [j_beg, j_end) of batch entry b, KV head kvh.
+  __device__ __forceinline__ void init(const __bf16* k, const ScoreGeom& g, int b, int kvh, int j_beg, int j_end) {
+    const uint32_t row_bytes = (uint32_t)g.Hkv * D * 2;
+    // The view is wave-uniform; pinning its parts to scalar registers keeps the compiler
+    // from wrapping every load in a loop over distinct views.
+    const uint64_t addr = reinterpret_cast<uint64_t>(k + (((int64_t)b * g.L + j_beg) * g.Hkv + kvh) * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    char* base = reinterpret_cast<char*>(((uint64_t)hi << 32) | lo);
+    // Up to the end of the chunk's last row's own D values.
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((j_end - j_beg - 1) * row_bytes + 2 * D);
+    rows = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, SCORE_BUF_FLAGS);
+    tile_bytes = SBN * row_bytes;
+    last_tile = (j_end - j_beg - 1) / SBN;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int e = threadIdx.x + 256 * i;
-      lrow[i] = e / CPR;
-      lch[i] = e % CPR;
-      soff[i] = lrow[i] * KP + lch[i] * 16;
+      const int lrow = e / CPR, lch = e % CPR;
+      loff[i] = (uint32_t)lrow * row_bytes + lch * 16;
+      soff[i] = lrow * KP + lch * 16;
     }
   }
-  // Rows past the sequence repeat its last row (their keys are masked by the callers).
-  __device__ __forceinline__ void load(int set, int j0) {
+  // Tile t of the chunk (keys j_beg + 64 t ...).
+  __device__ __forceinline__ void load(int set, int t) {
+    const uint32_t toff = (uint32_t)min(t, last_tile) * tile_bytes;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      st[set][i] = ld16(base + (int64_t)min(j0 + lrow[i], L - 1) * row_bytes + lch[i] * 16);
+    for (int i = 0; i < LPT; ++i) st[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rows, loff[i] + toff, 0, 0);
   }
   __device__ __forceinline__ void store(int set, char* lds) {
 #pragma unroll
@@ -417,13 +453,17 @@ __global__ __launch_bounds__(256, 2) void score_pass1_k16_kernel(const __bf16* _
   };
 
   KStage<D, KP, NS> ks;
-  ks.init(k, g, b, kvh);
+  ks.init(k, g, b, kvh, j_beg, j_end);
+  // Tiles in order (the loop waits for the oldest set only if the sets were issued in order).
 #pragma unroll
-  for (int i = 0; i < NS; ++i) ks.load(i, j_beg + i * SBN);
+  for (int i = 0; i < NS; ++i) {
+    ks.load(i, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   auto step = [&](int t, char* tile, int set) __attribute__((always_inline)) {
     ks.store(set, tile);
     __syncthreads();
-    ks.load(set, j_beg + (t + NS) * SBN);
+    ks.load(set, t + NS);
     if (!active || t >= nt) return;
     const int j0t = j_beg + t * SBN;
     auto blocks = [&](auto mask_tag) __attribute__((always_inline)) {
@@ -544,13 +584,17 @@ __global__ __launch_bounds__(256, 2) void score_pass2_k16_kernel(const __bf16* _
   };
 
   KStage<D, KP, NS> ks;
-  ks.init(k, g, b, kvh);
+  ks.init(k, g, b, kvh, j_beg, j_end);
+  // Tiles in order (the loop waits for the oldest set only if the sets were issued in order).
 #pragma unroll
-  for (int i = 0; i < NS; ++i) ks.load(i, j_beg + i * SBN);
+  for (int i = 0; i < NS; ++i) {
+    ks.load(i, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   auto step = [&](int t, char* tile, int set) __attribute__((always_inline)) {
     ks.store(set, tile);
     __syncthreads();
-    ks.load(set, j_beg + (t + NS) * SBN);
+    ks.load(set, t + NS);
     if (!active || t >= nt) return;
     const int j0t = j_beg + t * SBN;
     auto blocks = [&](auto mask_tag) __attribute__((always_inline)) {
@@ -608,7 +652,8 @@ hipError_t launch_score_t(const tsa_desc& d, const void* q, const void* k, float
       case 3: score_pass1_k16_kernel<D, 3><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
       default: score_pass1_k16_kernel<D, 4><<<blocks, 256, 0, s>>>(qb, kb, part, g, c); break;
     }
-    score_merge_kernel<<<d.B * d.H, 64 * MERGE_PARTS, 0, s>>>(part, stat, g.nchunk, g.Wp);
+    score_merge_kernel<<<d.B * d.H * ((g.Wp + MERGE_ROWS - 1) / MERGE_ROWS), MERGE_ROWS * MERGE_SLICES, 0, s>>>(
+        part, stat, g.nchunk, g.Wp);
     switch ((g.Wp + 15) / 16) {
       case 1: score_pass2_k16_kernel<D, 1><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
       case 2: score_pass2_k16_kernel<D, 2><<<blocks, 256, 0, s>>>(qb, kb, stat, scores, g, c); break;
@@ -624,7 +669,8 @@ hipError_t launch_score_t(const tsa_desc& d, const void* q, const void* k, float
   } else {
     score_pass1_kernel<T, D, 1><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, part, g, c);
   }
-  score_merge_kernel<<<d.B * d.H, 64 * MERGE_PARTS, 0, s>>>(part, stat, g.nchunk, g.Wp);
+  score_merge_kernel<<<d.B * d.H * ((g.Wp + MERGE_ROWS - 1) / MERGE_ROWS), MERGE_ROWS * MERGE_SLICES, 0, s>>>(
+        part, stat, g.nchunk, g.Wp);
   if (g.Wp > 32) {
     score_pass2_kernel<T, D, 2><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, stat, scores, g, c);
   } else {
