@@ -787,10 +787,16 @@ __global__ __launch_bounds__(NW * TSA_WAVE, 2) void attn_bf16_kernel(AttnParams 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kk][qb] = f32x4{};
+        // The score products issue at a raised wave priority: when both waves of a SIMD
+        // are ready, the one starting its burst of products goes first and the other's
+        // softmax arithmetic fills in behind it (about 1% faster at L = 131072 and 32768;
+        // the same over the PV products as well, or over the softmax, was slower).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < ST; ++st)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kk][qb] = mfma16(s[kk][qb], kf[st], qf[qb][st]);
+        __builtin_amdgcn_s_setprio(0);
       }
       if (kh + 31 > wrow0) {                       // the half reaches the diagonal
 #pragma unroll
