@@ -365,11 +365,15 @@ __device__ __forceinline__ f32x4 mfma16s(f32x4 c, bf16x8 a, bf16x8 b) {
 }
 
 // Both passes are software-pipelined over 16-key blocks: the products of block kb are
-// issued interleaved with the softmax arithmetic of block kb - 1 (one matrix instruction,
-// then three vector instructions, as scheduling groups), so a wave keeps the matrix cores
-// and its vector unit busy at once.  The causal mask is evaluated only in steps whose
-// blocks reach the window rows (a step processes block 3 of the previous tile and blocks
-// 0-2 of its own).
+// issued with the softmax arithmetic of block kb - 1, at a raised wave priority, so that of
+// the two waves of a SIMD the one with matrix work ready issues first and the other's
+// vector work fills in behind it.  Pass 1 issues the 16 products as one burst at the raised
+// priority and the softmax after it; pass 2 interleaves them (one matrix instruction, then
+// three vector instructions, as scheduling groups) and raises the priority over the whole
+// group.  Of the four arrangements (interleaved or not, with or without the priority) these
+// measured fastest: L = 131072, pass 1 79.2 -> 75.5 us, pass 2 81.6 -> 79.2 us.  The causal
+// mask is evaluated only in steps whose blocks reach the window rows (a step processes
+// block 3 of the previous tile and blocks 0-2 of its own).
 
 // Sixteen groups of one matrix instruction followed by three vector instructions.
 __device__ __forceinline__ void interleave_mfma_valu() {
@@ -476,12 +480,15 @@ __global__ __launch_bounds__(256, 2) void score_pass1_k16_kernel(const __bf16* _
         f32x4 acc[RB];
 #pragma unroll
         for (int qb = 0; qb < RB; ++qb) acc[qb] = f32x4{};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < ST; ++st)
 #pragma unroll
           for (int qb = 0; qb < RB; ++qb) acc[qb] = mfma16s(acc[qb], kf[st], qf[qb][st]);   // rows: keys, cols: queries
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         softmax_prev(mask_tag);
-        interleave_mfma_valu();
         guard_prev();
 #pragma unroll
         for (int qb = 0; qb < RB; ++qb) pacc[qb] = acc[qb];
@@ -607,12 +614,16 @@ __global__ __launch_bounds__(256, 2) void score_pass2_k16_kernel(const __bf16* _
         f32x4 acc[RB];
 #pragma unroll
         for (int qb = 0; qb < RB; ++qb) acc[qb] = f32x4{};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < ST; ++st)
 #pragma unroll
           for (int qb = 0; qb < RB; ++qb) acc[qb] = mfma16s(acc[qb], qf[qb][st], kf[st]);   // rows: queries, cols: keys
         auto finish = colsum_prev(mask_tag);
         interleave_mfma_valu();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         finish();
 #pragma unroll
         for (int qb = 0; qb < RB; ++qb) pacc[qb] = acc[qb];
