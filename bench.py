@@ -115,9 +115,11 @@ def stats(ms):
 
 
 # HBM bytes per launch of the fused attention kernel, from the committed rocprofv3
-# FETCH_SIZE / WRITE_SIZE summary, valid while the kernel sources hash as recorded there.
+# FETCH_SIZE / WRITE_SIZE summary, valid while the kernel sources and the build script (its
+# compiler flags) hash as recorded there.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fused_bf16_L128k_r0.5_hbm_traffic.txt")
-ATTN_SOURCES = ["token_sparse_attention_head_amd/csrc/attn.hip", "token_sparse_attention_head_amd/csrc/common.h"]
+ATTN_SOURCES = ["token_sparse_attention_head_amd/csrc/attn.hip", "token_sparse_attention_head_amd/csrc/common.h",
+                "token_sparse_attention_head_amd/build.py"]
 
 
 def attn_source_sha():
