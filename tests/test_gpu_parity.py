@@ -164,7 +164,9 @@ def test_compact_with_keep_all_equals_dense():
                                               # d = 64 with 64 window rows, many chunks with a ragged end, L = 1
                                               ("bf16", 128, 1, 16, 2, 1500, 64), ("bf16", 128, 2, 6, 2, 700, 40),
                                               ("bf16", 64, 1, 4, 2, 3001, 64), ("bf16", 128, 1, 2, 1, 20000, 64),
-                                              ("bf16", 128, 1, 4, 1, 1, 64)])
+                                              ("bf16", 128, 1, 4, 1, 1, 64),
+                                              # d = 64 with one and three 16-row window blocks
+                                              ("bf16", 64, 1, 4, 2, 1000, 16), ("bf16", 64, 2, 8, 2, 1500, 40)])
 def test_score(dt, d, B, H, Hkv, L, W):
     x = workloads.small_random(B, H, Hkv, L, d, seed=13, dtype=dt)
     s = host(tsa.score(dev(x["q"], dt), dev(x["k"], dt), W))
