@@ -41,9 +41,10 @@ def setup_module(module):
     (1, 3, 131072, 13107, 64, 4, False),
     (1, 2, 131072, 65536, 64, 4, True),
     (1, 1, 70000, 5000, 17, 9, True),
-    # rows up to 16384 run the one-workgroup select (2, 8 and 16 positions per thread);
+    # rows up to 16384 run the one-workgroup select (2, 4, 8 and 16 positions per thread);
     # 16385 is the shortest row of the multi-workgroup path
     (1, 2, 2000, 700, 16, 2, True),
+    (1, 3, 3500, 1000, 64, 4, True),
     (2, 2, 5000, 1300, 64, 4, False),
     (1, 2, 9000, 4500, 64, 4, True),
     (1, 3, 16384, 4096, 64, 4, False),
