@@ -56,5 +56,45 @@ def check_selection(s_or, idx_gpu, keep, W, n_sink, rel=1e-6):
     return n_diff
 
 
+def check_adaptive_selection(s_or, idx_gpu, keep, W, n_sink, tau, rel=3e-5):
+    """Token-coverage rule end to end, on float64 scores [B,H,L] and the GPU's padded subsets
+    [B,H,keep]: per row, one more position leaving (the lowest-scoring non-forced member,
+    ties to the higher position) would take the mass that left (every non-member) above tau
+    of the row's total; below the cap (K < keep) the mass that left is within it (at the cap
+    more leaves than coverage alone asks); both up to a relative slack `rel` (the GPU decides
+    on its fp32 scores).  The members are the K best positions up to near-ties at the
+    K-threshold (as in check_selection).  Returns the number of near-tie differences."""
+    B, H, L = s_or.shape
+    F = set(oracle.forced_positions(L, W, n_sink).tolist())
+    tau32 = float(np.float32(tau))
+    n_diff = 0
+    for b in range(B):
+        for h in range(H):
+            row = np.asarray(s_or[b, h], dtype=np.float64)
+            S = [int(p) for p in idx_gpu[b, h] if p >= 0]
+            K = len(S)
+            assert all(p < 0 for p in idx_gpu[b, h][K:]), "padding only after the members"
+            assert all(x < y for x, y in zip(S, S[1:])) and F <= set(S)
+            member = np.zeros(L, dtype=bool)
+            member[S] = True
+            budget = tau32 * row.sum()
+            left = row[~member].sum()
+            if K < keep:
+                assert left <= budget * (1 + rel), (b, h, left, budget)
+            movable = [p for p in S if p not in F]
+            if movable:
+                nxt = min(movable, key=lambda p: (row[p], -p))
+                assert left + row[nxt] > budget * (1 - rel), (b, h, left, row[nxt], budget)
+            S_or = set(oracle.select_row(row, K, W, n_sink).tolist())
+            diff = S_or.symmetric_difference(S)
+            if diff:
+                theta = oracle.threshold(row, K, W, n_sink)
+                for p in diff:
+                    assert p not in F
+                    assert abs(row[p] - theta) <= rel * theta, (b, h, p, row[p], theta)
+                n_diff += len(diff)
+    return n_diff
+
+
 def rel_err(gpu, ref, floor=1e-30):
     return float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), floor)))

@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads
 from tests._lib import ensure_built
-from tests.gpu_helpers import TOL, dev, half_ulp, host, rel_err, round_to
+from tests.gpu_helpers import TOL, check_adaptive_selection, dev, half_ulp, host, rel_err, round_to
 
 pytestmark = pytest.mark.gpu
 
@@ -125,9 +125,12 @@ def _end_to_end(x, dt, keep, W, ns, tau, in_place=False, per_kv_head=False, scal
     idx = ig.cpu().numpy().astype(np.int64)
     d = x["q"].shape[-1]
     sc = scale if scale > 0 else 1.0 / np.sqrt(d)
-    assert rel_err(s32.astype(np.float64), oracle.score(x["q"], x["k"], W, sc)) <= 1e-5
+    s64 = oracle.score(x["q"], x["k"], W, sc)
+    assert rel_err(s32.astype(np.float64), s64) <= 1e-5
     # budgets and subsets bit-exact on the GPU's own scores
     assert np.array_equal(idx, oracle.select(s32, keep, W, ns, kvh, tau))
+    # and valid under the coverage rule on the float64 scores (per KV head: their sums)
+    n_tie = check_adaptive_selection(oracle.group_scores(s64, Hkv) if per_kv_head else s64, idx, keep, W, ns, tau)
     ks = (idx >= 0).sum(axis=-1)
     qh, kh, vh = oracle.gather(x["q"], x["k"], x["v"], idx)
     want = oracle.scatter_residual(oracle.attend(qh, kh, vh, sc), idx, x["r"])
@@ -142,7 +145,7 @@ def _end_to_end(x, dt, keep, W, ns, tau, in_place=False, per_kv_head=False, scal
     assert np.array_equal(got[~sel], x["r"][~sel].astype(np.float64))
     excess = np.abs(got[sel] - want[sel]) - half_ulp(got[sel], dt)
     print(f"adaptive {dt} tau={tau}{' per KV head' if per_kv_head else ''}: K {ks.min()}..{ks.max()} of cap "
-          f"{keep}, excess over half-ulp {excess.max():.3e}")
+          f"{keep}, near-tie differences from float64 {n_tie}, excess over half-ulp {excess.max():.3e}")
     assert excess.max() <= TOL[dt]
     return out, idx
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads
 from tests._lib import ensure_built
-from tests.gpu_helpers import TOL, check_selection, half_ulp, rel_err
+from tests.gpu_helpers import TOL, check_adaptive_selection, check_selection, half_ulp, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -187,6 +187,12 @@ def test_full_adaptive_graded_L128k():
     idx_all = ig.cpu().numpy().astype(np.int64)
     # budgets and subsets of every head bit-exact on the GPU's own scores
     assert np.array_equal(idx_all, oracle.select(s32, w.keep, w.W, w.n_sink, tau=w.tau))
+    # and valid under the coverage rule on float64 scores, on heads from diffuse to sharp
+    heads = [0, 10, 21, 31]
+    s_or = np.stack([oracle.score_head(x["q"][0, :, h, :].astype(np.float64), x["k"][0, :, h // G, :].astype(np.float64),
+                                       w.W, scale) for h in heads])[None]
+    n_tie = check_adaptive_selection(s_or, idx_all[:, heads], w.keep, w.W, w.n_sink, w.tau)
+    print(f"{w.name}: near-tie differences from float64 scores on heads {heads}: {n_tie}")
     ks = (idx_all >= 0).sum(axis=-1)
     print(f"{w.name}: K/L per head {ks.min() / L:.3f} .. {ks.max() / L:.3f}, mean {ks.mean() / L:.3f}")
     assert ks[0, 0] > ks[0, -1]                    # sharper heads keep fewer positions
